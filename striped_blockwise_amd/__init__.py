@@ -1,0 +1,272 @@
+"""Python binding of libra.so: blockwise Ring / Striped attention on MI355X (gfx950).
+
+Argument marshalling only.  Every step of the computation runs in the HIP kernels behind the
+C ABI (include/ra.h); PyTorch provides device memory and the current stream.  There is no
+fallback: if libra.so is missing or the tensors are not on a GPU the calls raise.
+
+Layout names: "contiguous" (device p owns tokens [p*c, (p+1)*c); Ring Attention review, step 1)
+and "striped" (device p owns tokens p, p+P, ...; Striped Attention review, "分区策略对比").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "CONTIGUOUS", "STRIPED", "BF16", "F32", "lib", "abi_version", "check", "tile_shape",
+    "permute", "permute_ids", "round", "merge", "forward", "new_stats", "RaError",
+]
+
+CONTIGUOUS, STRIPED = 0, 1
+BF16, F32 = 0, 1
+RA_OK, RA_E_INVAL, RA_E_UNSUPPORTED, RA_E_HIP = 0, -1, -2, -3
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libra.so")
+_lib = None
+
+
+class RaError(RuntimeError):
+    """Raised for a non-zero status of the C ABI."""
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("n", ctypes.c_int64),
+                ("d", ctypes.c_int64), ("P", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("layout", ctypes.c_int32), ("causal", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+_P = ctypes.POINTER(_Problem)
+_vp = ctypes.c_void_p
+_i32, _i64 = ctypes.c_int32, ctypes.c_int64
+
+_SIGS = {
+    "ra_abi_version": (_i32, []),
+    "ra_last_error": (ctypes.c_char_p, []),
+    "ra_check": (_i32, [_P, _i32, _i32]),
+    "ra_tile_shape": (_i32, [_i32, _i64, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
+    "ra_permute": (_i32, [_vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp]),
+    "ra_permute_ids": (_i32, [_vp, _vp, _i64, _i32, _i32, _vp]),
+    "ra_round": (_i32, [_P, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "ra_merge": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _vp]),
+    "ra_forward": (_i32, [_P, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _vp, _vp]),
+}
+
+
+def lib():
+    """Load libra.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RaError(f"{_LIB_PATH} not found: build it with `python -m striped_blockwise_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def _raise(status: int, what: str):
+    if status == RA_OK:
+        return
+    msg = lib().ra_last_error().decode(errors="replace")
+    if status == RA_E_INVAL:
+        raise ValueError(f"{what}: {msg}")
+    if status == RA_E_UNSUPPORTED:
+        raise NotImplementedError(f"{what}: {msg}")
+    raise RaError(f"{what} (status {status}): {msg}")
+
+
+def _layout(x) -> int:
+    if isinstance(x, str):
+        return {"contiguous": CONTIGUOUS, "ring": CONTIGUOUS, "striped": STRIPED}[x]
+    return int(x)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return BF16
+    if dt == torch.float32:
+        return F32
+    raise ValueError(f"unsupported dtype {dt} (bfloat16 or float32)")
+
+
+def _problem(B, H, n, d, P, dtype, layout, causal, scale) -> _Problem:
+    return _Problem(int(B), int(H), int(n), int(d), int(P), int(dtype), _layout(layout),
+                    1 if causal else 0, float(scale))
+
+
+def _gpu(*ts: torch.Tensor):
+    dev = ts[0].device
+    for t in ts:
+        if t.device.type != "cuda":
+            raise ValueError("tensors must be on a GPU (device 'cuda')")
+        if t.device != dev:
+            raise ValueError("tensors must be on the same GPU")
+    return dev
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def abi_version() -> int:
+    return int(lib().ra_abi_version())
+
+
+def check(B, H, n, d, P, dtype=BF16, layout=CONTIGUOUS, causal=True, scale=0.0, p=0, kv=0) -> None:
+    """Host-only validation (no GPU needed); raises on a bad problem."""
+    pr = _problem(B, H, n, d, P, dtype, layout, causal, scale)
+    _raise(lib().ra_check(ctypes.byref(pr), int(p), int(kv)), "ra_check")
+
+
+def tile_shape(dtype=BF16, d=128):
+    tq, tk = _i32(), _i32()
+    _raise(lib().ra_tile_shape(int(dtype), int(d), ctypes.byref(tq), ctypes.byref(tk)), "ra_tile_shape")
+    return tq.value, tk.value
+
+
+def permute(x: torch.Tensor, P: int, dim: int = -2, inverse: bool = False, out=None) -> torch.Tensor:
+    """Striped permutation of the token axis ``dim`` of a contiguous GPU tensor.
+
+    inverse=False: token order -> striped layout; inverse=True: striped layout -> token order.
+    """
+    _gpu(x)
+    if not x.is_contiguous():
+        raise ValueError("permute needs a contiguous tensor")
+    dim = dim % x.dim()
+    n = x.shape[dim]
+    BH = 1
+    for s in x.shape[:dim]:
+        BH *= s
+    row = x.element_size()
+    for s in x.shape[dim + 1:]:
+        row *= s
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError("out must match x (shape, dtype) and be contiguous")
+    _gpu(x, out)
+    with torch.cuda.device(x.device):
+        _raise(lib().ra_permute(_ptr(x), _ptr(out), BH, n, row, int(P), 1 if inverse else 0,
+                                _vp(_stream(x.device))), "ra_permute")
+    return out
+
+
+def permute_ids(ids: torch.Tensor, P: int, inverse: bool = False, out=None) -> torch.Tensor:
+    """Striped permutation of an int64 position-ID vector."""
+    _gpu(ids)
+    if ids.dtype != torch.int64 or ids.dim() != 1 or not ids.is_contiguous():
+        raise ValueError("ids must be a contiguous 1-D int64 tensor")
+    out = torch.empty_like(ids) if out is None else out
+    _gpu(ids, out)
+    with torch.cuda.device(ids.device):
+        _raise(lib().ra_permute_ids(_ptr(ids), _ptr(out), ids.numel(), int(P), 1 if inverse else 0,
+                                    _vp(_stream(ids.device))), "ra_permute_ids")
+    return out
+
+
+def _block_strides(t: torch.Tensor, name: str):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, H, c, d]")
+    B, H, c, d = t.shape
+    if t.stride(3) != 1 or (c > 1 and t.stride(2) != d):
+        raise ValueError(f"{name}: rows must be contiguous (strides [.., .., d, 1])")
+    if B * H > 1 and H > 1 and B > 1 and t.stride(0) != H * t.stride(1):
+        raise ValueError(f"{name}: (b, h) matrices must be evenly strided")
+    return t.stride(1) if H > 1 else (t.stride(0) if B > 1 else c * d)
+
+
+def new_stats(P: int, device="cuda") -> torch.Tensor:
+    """Zeroed device buffer of [P, P] ra_round_stats_t (4 uint64 each, as int64)."""
+    return torch.zeros((P, P, 4), dtype=torch.int64, device=device)
+
+
+def round(q_blk, k_blk, v_blk, P: int, p: int, kv: int, layout="contiguous", causal=True,
+          scale: float = 0.0, stats=None, out=None):
+    """One ring round: device p's query block against K/V block kv.
+
+    q_blk, k_blk, v_blk: [B, H, c, d] views (bf16 or f32), rows contiguous (views into full
+    [B, H, n, d] tensors are fine).  Returns (o_part [B,H,c,d] f32, lse_part [B,H,c] f32).
+    stats: None or an int64 tensor with >= 4 elements (one ra_round_stats_t) to add counts to.
+    """
+    dev = _gpu(q_blk, k_blk, v_blk)
+    B, H, c, d = q_blk.shape
+    if k_blk.shape != q_blk.shape or v_blk.shape != q_blk.shape:
+        raise ValueError("q, k, v blocks must have the same shape")
+    if not (q_blk.dtype == k_blk.dtype == v_blk.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    sq = _block_strides(q_blk, "q")
+    sk = _block_strides(k_blk, "k")
+    sv = _block_strides(v_blk, "v")
+    if sk != sv:
+        raise ValueError("k and v must have the same (b, h) stride")
+    if out is None:
+        o = torch.empty((B, H, c, d), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, H, c), dtype=torch.float32, device=dev)
+    else:
+        o, lse = out
+    if stats is not None and (stats.dtype != torch.int64 or stats.numel() < 4 or not stats.is_contiguous()):
+        raise ValueError("stats must be a contiguous int64 tensor of >= 4 elements")
+    pr = _problem(B, H, c * P, d, P, _dtype_code(q_blk.dtype), layout, causal, scale)
+    with torch.cuda.device(dev):
+        _raise(lib().ra_round(ctypes.byref(pr), _ptr(q_blk), _ptr(k_blk), _ptr(v_blk), sq, sk,
+                              int(p), int(kv), _ptr(o), _ptr(lse), _ptr(stats), _vp(_stream(dev))),
+               "ra_round")
+    return o, lse
+
+
+def merge(o_acc, lse_acc, o_part, lse_part) -> None:
+    """In-place log-sum-exp merge of a round partial into (o_acc, lse_acc); float32, contiguous."""
+    _gpu(o_acc, lse_acc, o_part, lse_part)
+    for t in (o_acc, lse_acc, o_part, lse_part):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("merge operands must be contiguous float32")
+    d = o_acc.shape[-1]
+    rows = lse_acc.numel()
+    if o_acc.numel() != rows * d or o_part.shape != o_acc.shape or lse_part.shape != lse_acc.shape:
+        raise ValueError("shape mismatch between accumulator and partial")
+    with torch.cuda.device(o_acc.device):
+        _raise(lib().ra_merge(_ptr(o_acc), _ptr(lse_acc), _ptr(o_part), _ptr(lse_part), rows, d,
+                              _vp(_stream(o_acc.device))), "ra_merge")
+
+
+def forward(q, k, v, P: int, layout="contiguous", causal=True, p_begin: int = 0, p_end=None,
+            o_dtype=None, want_lse: bool = True, scale: float = 0.0, stats=None, out=None):
+    """All P rounds for devices [p_begin, p_end), fused in one launch.
+
+    q, k, v: contiguous [B, H, n, d] in layout order.  Returns (o, lse): o is
+    [B, H, (p_end-p_begin)*c, d] in o_dtype (default: q's dtype), lse the matching float32
+    log-sum-exp (None if want_lse is False).  stats: None or new_stats(P).
+    """
+    dev = _gpu(q, k, v)
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must be [B, H, n, d] of one shape")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    B, H, n, d = q.shape
+    p_end = P if p_end is None else p_end
+    c = n // P if P > 0 else 0
+    rows = max(0, p_end - p_begin) * c
+    o_dtype = q.dtype if o_dtype is None else o_dtype
+    if out is None:
+        o = torch.empty((B, H, rows, d), dtype=o_dtype, device=dev)
+        lse = torch.empty((B, H, rows), dtype=torch.float32, device=dev) if want_lse else None
+    else:
+        o, lse = out
+    if stats is not None and (stats.dtype != torch.int64 or stats.numel() < P * P * 4 or not stats.is_contiguous()):
+        raise ValueError("stats must be new_stats(P)")
+    pr = _problem(B, H, n, d, P, _dtype_code(q.dtype), layout, causal, scale)
+    with torch.cuda.device(dev):
+        _raise(lib().ra_forward(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), int(p_begin), int(p_end),
+                                _ptr(o), _dtype_code(o_dtype), _ptr(lse), _ptr(stats), _vp(_stream(dev))),
+               "ra_forward")
+    return o, lse

@@ -1,0 +1,217 @@
+// Host side of libra.so: argument validation, error reporting and kernel dispatch for the C ABI
+// declared in include/ra.h.  Nothing here allocates device memory or synchronizes.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "ra_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ra_status_t fail(ra_status_t code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+ra_status_t ok() {
+  g_err[0] = '\0';
+  return RA_OK;
+}
+
+ra_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(RA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int64_t elem_bytes(int32_t dtype) { return dtype == RA_F32 ? 4 : 2; }
+
+bool empty_problem(const ra_problem_t* pr) { return pr->B == 0 || pr->H == 0 || pr->n == 0; }
+
+// Problem-level checks shared by every attention entry point.
+ra_status_t check_problem(const ra_problem_t* pr) {
+  if (!pr) return fail(RA_E_INVAL, "problem pointer is NULL");
+  if (pr->B < 0 || pr->H < 0 || pr->n < 0) return fail(RA_E_INVAL, "B, H and n must be >= 0");
+  if (pr->d <= 0) return fail(RA_E_INVAL, "head dim d must be > 0 (got %lld)", (long long)pr->d);
+  if (pr->P < 1) return fail(RA_E_INVAL, "P must be >= 1 (got %d)", pr->P);
+  if (pr->n % pr->P != 0)
+    return fail(RA_E_INVAL, "n (%lld) must be a multiple of P (%d)", (long long)pr->n, pr->P);
+  if (pr->dtype != RA_BF16 && pr->dtype != RA_F32) return fail(RA_E_INVAL, "unknown dtype %d", pr->dtype);
+  if (pr->layout != RA_CONTIGUOUS && pr->layout != RA_STRIPED)
+    return fail(RA_E_INVAL, "unknown layout %d", pr->layout);
+  if (pr->causal != 0 && pr->causal != 1) return fail(RA_E_INVAL, "causal must be 0 or 1");
+  if (!std::isfinite(pr->scale)) return fail(RA_E_INVAL, "scale must be finite");
+  const int64_t c = pr->n / pr->P;
+  if (c > (int64_t)INT32_MAX / pr->d || pr->B > INT32_MAX || pr->H > INT32_MAX ||
+      pr->B * pr->H > INT32_MAX / 64)
+    return fail(RA_E_INVAL, "problem too large: rows per block x d must fit in int32");
+  if (pr->B > 0 && pr->H > 0 && pr->n > INT64_MAX / pr->B / pr->H / pr->d)
+    return fail(RA_E_INVAL, "problem too large: B*H*n*d overflows int64");
+  const bool sup = pr->dtype == RA_BF16 ? ra::attn_bf16_supported(pr->d) : ra::attn_f32_supported(pr->d);
+  if (!sup)
+    return fail(RA_E_UNSUPPORTED, "head dim %lld is not supported for %s inputs (bf16: 128; f32: 32, 64, 128)",
+                (long long)pr->d, pr->dtype == RA_BF16 ? "bf16" : "f32");
+  return ok();
+}
+
+float eff_scale(const ra_problem_t* pr) {
+  return pr->scale > 0.f ? pr->scale : (float)(1.0 / std::sqrt((double)pr->d));
+}
+
+ra_status_t launch_attn(const ra_problem_t* pr, const ra::AttnArgs& a, hipStream_t s) {
+  hipError_t e = pr->dtype == RA_BF16 ? ra::launch_attn_bf16(a, (int)pr->d, s)
+                                      : ra::launch_attn_f32(a, (int)pr->d, s);
+  return hip_status(e, "attention kernel launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ra_abi_version(void) { return RA_ABI_VERSION; }
+
+const char* ra_last_error(void) { return g_err; }
+
+ra_status_t ra_check(const ra_problem_t* prob, int32_t p, int32_t kv) {
+  ra_status_t st = check_problem(prob);
+  if (st != RA_OK) return st;
+  if (p < 0 || p >= prob->P) return fail(RA_E_INVAL, "query device p=%d out of range [0, %d)", p, prob->P);
+  if (kv < 0 || kv >= prob->P) return fail(RA_E_INVAL, "K/V device kv=%d out of range [0, %d)", kv, prob->P);
+  return ok();
+}
+
+ra_status_t ra_tile_shape(int32_t dtype, int64_t d, int32_t* tq, int32_t* tk) {
+  if (!tq || !tk) return fail(RA_E_INVAL, "tq / tk out-pointers must not be NULL");
+  if (dtype == RA_BF16) {
+    if (!ra::attn_bf16_supported(d)) return fail(RA_E_UNSUPPORTED, "bf16 head dim %lld not supported", (long long)d);
+    ra::attn_bf16_tile(tq, tk);
+  } else if (dtype == RA_F32) {
+    if (!ra::attn_f32_supported(d)) return fail(RA_E_UNSUPPORTED, "f32 head dim %lld not supported", (long long)d);
+    ra::attn_f32_tile(tq, tk);
+  } else {
+    return fail(RA_E_INVAL, "unknown dtype %d", dtype);
+  }
+  return ok();
+}
+
+ra_status_t ra_permute(const void* src, void* dst, int64_t BH, int64_t n, int64_t row_bytes,
+                       int32_t P, int32_t inverse, void* stream) {
+  if (BH < 0 || n < 0) return fail(RA_E_INVAL, "BH and n must be >= 0");
+  if (P < 1) return fail(RA_E_INVAL, "P must be >= 1 (got %d)", P);
+  if (n % P != 0) return fail(RA_E_INVAL, "n (%lld) must be a multiple of P (%d)", (long long)n, P);
+  if (row_bytes <= 0 || row_bytes % 4 != 0) return fail(RA_E_INVAL, "row_bytes must be a positive multiple of 4");
+  if (n > (int64_t)UINT32_MAX / 2) return fail(RA_E_INVAL, "n too large");
+  if (BH == 0 || n == 0) return ok();
+  if (!src || !dst) return fail(RA_E_INVAL, "src / dst must not be NULL");
+  if (!aligned(src, 4) || !aligned(dst, 4)) return fail(RA_E_INVAL, "src / dst must be 4-byte aligned");
+  if (BH > INT64_MAX / n / row_bytes) return fail(RA_E_INVAL, "BH*n*row_bytes overflows");
+  const int64_t bytes = BH * n * row_bytes;
+  const char* s0 = (const char*)src;
+  const char* d0 = (const char*)dst;
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return fail(RA_E_INVAL, "src and dst overlap");
+  return hip_status(ra::launch_permute(src, dst, BH, n, row_bytes, P, inverse ? 1 : 0, (hipStream_t)stream),
+                    "permute kernel launch");
+}
+
+ra_status_t ra_permute_ids(const int64_t* src, int64_t* dst, int64_t n, int32_t P, int32_t inverse,
+                           void* stream) {
+  return ra_permute(src, dst, 1, n, 8, P, inverse, stream);
+}
+
+ra_status_t ra_round(const ra_problem_t* prob, const void* q, const void* k, const void* v,
+                     int64_t q_stride_bh, int64_t kv_stride_bh, int32_t p, int32_t kv,
+                     float* o_part, float* lse_part, ra_round_stats_t* stats, void* stream) {
+  ra_status_t st = ra_check(prob, p, kv);
+  if (st != RA_OK) return st;
+  if (empty_problem(prob)) return ok();
+  const int64_t c = prob->n / prob->P;
+  const int64_t d = prob->d;
+  if (!q || !k || !v || !o_part || !lse_part) return fail(RA_E_INVAL, "q, k, v, o_part and lse_part must not be NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o_part, 16) || !aligned(lse_part, 4))
+    return fail(RA_E_INVAL, "q, k, v and o_part must be 16-byte aligned, lse_part 4-byte aligned");
+  const int64_t vec = 16 / elem_bytes(prob->dtype);
+  if (q_stride_bh < 0 || kv_stride_bh < 0 || q_stride_bh % vec || kv_stride_bh % vec)
+    return fail(RA_E_INVAL, "strides must be >= 0 and multiples of %lld elements", (long long)vec);
+  if (prob->B * prob->H > 1 && (q_stride_bh < c * d || kv_stride_bh < c * d))
+    return fail(RA_E_INVAL, "strides must be at least c*d = %lld elements", (long long)(c * d));
+  if (stats && !aligned(stats, 8)) return fail(RA_E_INVAL, "stats must be 8-byte aligned");
+  ra::AttnArgs a{};
+  a.q = q; a.k = k; a.v = v;
+  a.q_bh_stride = q_stride_bh; a.kv_bh_stride = kv_stride_bh;
+  a.q_dev_stride = 0; a.kv_blk_stride = 0;
+  a.o = o_part; a.lse = lse_part;
+  a.o_bh_stride = c * d; a.lse_bh_stride = c;
+  a.c = (int)c; a.P = prob->P; a.BH = (int)(prob->B * prob->H);
+  a.p_begin = p; a.n_dev = 1; a.kv_base = kv;
+  a.r_begin = ra::ring_block(p, kv, prob->P);   // (p - kv) mod P: the round that brings block kv
+  a.r_count = 1;
+  a.layout = prob->layout; a.causal = prob->causal;
+  a.scale = eff_scale(prob);
+  a.o_f32 = 1;
+  a.stats = stats; a.stats_single = 1;
+  return launch_attn(prob, a, (hipStream_t)stream);
+}
+
+ra_status_t ra_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
+                     int64_t rows, int64_t d, void* stream) {
+  if (rows < 0 || d <= 0) return fail(RA_E_INVAL, "rows must be >= 0 and d > 0");
+  if (rows == 0) return ok();
+  if (!o_acc || !lse_acc || !o_part || !lse_part) return fail(RA_E_INVAL, "pointers must not be NULL");
+  if (!aligned(o_acc, 4) || !aligned(lse_acc, 4) || !aligned(o_part, 4) || !aligned(lse_part, 4))
+    return fail(RA_E_INVAL, "pointers must be 4-byte aligned");
+  if (d % 4 == 0 && (!aligned(o_acc, 16) || !aligned(o_part, 16)))
+    return fail(RA_E_INVAL, "o_acc / o_part must be 16-byte aligned when d %% 4 == 0");
+  if (rows > INT64_MAX / d / 4) return fail(RA_E_INVAL, "rows*d overflows");
+  const char* a0 = (const char*)o_acc;
+  const char* b0 = (const char*)o_part;
+  const int64_t ob = rows * d * 4;
+  if (a0 < b0 + ob && b0 < a0 + ob) return fail(RA_E_INVAL, "o_part overlaps o_acc");
+  if ((const char*)lse_acc < (const char*)lse_part + rows * 4 && (const char*)lse_part < (const char*)lse_acc + rows * 4)
+    return fail(RA_E_INVAL, "lse_part overlaps lse_acc");
+  return hip_status(ra::launch_merge(o_acc, lse_acc, o_part, lse_part, rows, d, (hipStream_t)stream),
+                    "merge kernel launch");
+}
+
+ra_status_t ra_forward(const ra_problem_t* prob, const void* q, const void* k, const void* v,
+                       int32_t p_begin, int32_t p_end, void* o, int32_t o_dtype, float* lse,
+                       ra_round_stats_t* stats, void* stream) {
+  ra_status_t st = check_problem(prob);
+  if (st != RA_OK) return st;
+  if (p_begin < 0 || p_end > prob->P || p_begin >= p_end)
+    return fail(RA_E_INVAL, "device range [%d, %d) must be non-empty inside [0, %d)", p_begin, p_end, prob->P);
+  if (o_dtype != RA_BF16 && o_dtype != RA_F32) return fail(RA_E_INVAL, "unknown o_dtype %d", o_dtype);
+  if (empty_problem(prob)) return ok();
+  if (!q || !k || !v || !o) return fail(RA_E_INVAL, "q, k, v and o must not be NULL");
+  const int64_t c = prob->n / prob->P;
+  const int64_t d = prob->d;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+    return fail(RA_E_INVAL, "q, k and v must be 16-byte aligned");
+  if (!aligned(o, o_dtype == RA_F32 ? 16 : 8) || (lse && !aligned(lse, 4)))
+    return fail(RA_E_INVAL, "o must be 16-byte (f32) or 8-byte (bf16) aligned, lse 4-byte aligned");
+  if (stats && !aligned(stats, 8)) return fail(RA_E_INVAL, "stats must be 8-byte aligned");
+  const int64_t ndev = p_end - p_begin;
+  ra::AttnArgs a{};
+  a.q = (const char*)q + (int64_t)p_begin * c * d * elem_bytes(prob->dtype);
+  a.k = k; a.v = v;
+  a.q_bh_stride = prob->n * d; a.kv_bh_stride = prob->n * d;
+  a.q_dev_stride = c * d; a.kv_blk_stride = c * d;
+  a.o = o; a.lse = lse;
+  a.o_bh_stride = ndev * c * d; a.lse_bh_stride = ndev * c;
+  a.c = (int)c; a.P = prob->P; a.BH = (int)(prob->B * prob->H);
+  a.p_begin = p_begin; a.n_dev = (int)ndev; a.kv_base = 0;
+  a.r_begin = 0; a.r_count = prob->P;
+  a.layout = prob->layout; a.causal = prob->causal;
+  a.scale = eff_scale(prob);
+  a.o_f32 = o_dtype == RA_F32 ? 1 : 0;
+  a.stats = stats; a.stats_single = 0;
+  return launch_attn(prob, a, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// Internal declarations shared by the HIP translation units of libra.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ra.h"
+
+namespace ra {
+
+// Per-(query device, K/V block) mask class.  From the causal matrix (query position < key
+// position is masked; Striped Attention review, "核心公式") and the GetMask procedures
+// ("GetMask 函数"), in local indices y (query row of block p) and x (key row of block k):
+//   FULL   every pair visible   (non-causal; contiguous block from an earlier device)
+//   INCL   visible iff x <= y   (contiguous own block; striped block from device k <= p)
+//   STRICT visible iff x <  y   (striped block from device k > p)
+//   SKIP   nothing visible      (contiguous block from a later device)
+enum Mode : int { MODE_FULL = 0, MODE_INCL = 1, MODE_STRICT = 2, MODE_SKIP = 3 };
+
+__host__ __device__ inline int round_mode(int layout, int causal, int p, int k) {
+  if (!causal) return MODE_FULL;
+  if (layout == RA_CONTIGUOUS) return k < p ? MODE_FULL : (k == p ? MODE_INCL : MODE_SKIP);
+  return k <= p ? MODE_INCL : MODE_STRICT;
+}
+
+// Ring schedule (Ring Attention review, step 2): blocks move from rank i to rank i+1 each
+// round, so in round r device p holds the block that started on device (p - r) mod P.
+__host__ __device__ inline int ring_block(int p, int r, int P) {
+  int k = (p - r) % P;
+  return k < 0 ? k + P : k;
+}
+
+// Launch description for the attention kernels (one for ra_round, one for ra_forward).
+struct AttnArgs {
+  const void* q;          // block of device p_begin (element type per kernel)
+  const void* k;          // K/V block kv_base
+  const void* v;
+  int64_t q_bh_stride;    // elements between consecutive (b, h) matrices of q
+  int64_t kv_bh_stride;   // same for k and v
+  int64_t q_dev_stride;   // elements between consecutive device blocks of q
+  int64_t kv_blk_stride;  // elements between consecutive K/V blocks
+  void* o;                // output rows of device p_begin, then p_begin+1, ...
+  float* lse;             // nullable
+  int64_t o_bh_stride;    // elements between (b, h) matrices of o
+  int64_t lse_bh_stride;  // elements between (b, h) vectors of lse
+  int c;                  // rows per block
+  int P;                  // devices
+  int BH;                 // B * H
+  int p_begin;            // absolute index of the first query device
+  int n_dev;              // number of query devices
+  int kv_base;            // block index the k / v pointers point at
+  int r_begin;            // first ring round
+  int r_count;            // number of rounds
+  int layout;
+  int causal;
+  float scale;            // score multiplier (natural units)
+  int o_f32;              // 1: o is float32, 0: bf16
+  ra_round_stats_t* stats;  // nullable
+  int stats_single;       // 1: one entry (ra_round), 0: [P][P] indexed [p][r]
+};
+
+hipError_t launch_permute(const void* src, void* dst, int64_t BH, int64_t n, int64_t row_bytes,
+                          int P, int inverse, hipStream_t s);
+hipError_t launch_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
+                        int64_t rows, int64_t d, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, int d, hipStream_t s);
+hipError_t launch_attn_bf16(const AttnArgs& a, int d, hipStream_t s);
+
+bool attn_f32_supported(int64_t d);
+bool attn_bf16_supported(int64_t d);
+void attn_f32_tile(int* tq, int* tk);
+void attn_bf16_tile(int* tq, int* tk);
+
+}  // namespace ra

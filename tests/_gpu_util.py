@@ -1,0 +1,51 @@
+"""Shared helpers for the GPU parity tests: tolerances, comparisons and skip logic."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+# Tolerances against the fp64 oracle on the identical (already rounded) inputs.
+F32_O_ABS = 1e-4          # float32 inputs: O max-abs
+F32_LSE_ABS = 1e-4        # float32 inputs: LSE max-abs
+BF16_O_ABS = 2e-2         # bf16 inputs: O max-abs
+BF16_O_RELFRO = 1e-2      # bf16 inputs: ||O - O_ref||_F / ||O_ref||_F
+BF16_LSE_ABS = 1e-3       # bf16 inputs: LSE max-abs
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import striped_blockwise_amd as ra
+    ra.lib()                                 # raises if libra.so is missing: no silent fallback
+
+
+def np64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def compare(o_gpu, lse_gpu, o_ref, lse_ref, kind: str, label: str = ""):
+    """Element-wise comparison; rows with reference LSE = -inf must be exactly (0, -inf)."""
+    o = np64(o_gpu) if isinstance(o_gpu, torch.Tensor) else np.asarray(o_gpu, np.float64)
+    lse = np64(lse_gpu) if isinstance(lse_gpu, torch.Tensor) else np.asarray(lse_gpu, np.float64)
+    o_ref = np.asarray(o_ref, np.float64)
+    lse_ref = np.asarray(lse_ref, np.float64)
+    assert o.shape == o_ref.shape, (label, o.shape, o_ref.shape)
+    assert lse.shape == lse_ref.shape, (label, lse.shape, lse_ref.shape)
+    empty = ~np.isfinite(lse_ref)
+    assert np.all(lse[empty] == -np.inf), f"{label}: empty rows must have LSE = -inf"
+    assert np.all(o[empty] == 0.0), f"{label}: empty rows must have O = 0"
+    live = ~empty
+    assert np.all(np.isfinite(lse[live])) and np.all(np.isfinite(o[live])), f"{label}: non-finite output"
+    err_o = float(np.abs(o[live] - o_ref[live]).max()) if live.any() else 0.0
+    err_l = float(np.abs(lse[live] - lse_ref[live]).max()) if live.any() else 0.0
+    if kind == "f32":
+        assert err_o <= F32_O_ABS, f"{label}: O max-abs {err_o:.3e} > {F32_O_ABS}"
+        assert err_l <= F32_LSE_ABS, f"{label}: LSE max-abs {err_l:.3e} > {F32_LSE_ABS}"
+    else:
+        num = float(np.linalg.norm((o - o_ref)[live]))
+        den = float(np.linalg.norm(o_ref[live])) or 1.0
+        assert err_o <= BF16_O_ABS, f"{label}: O max-abs {err_o:.3e} > {BF16_O_ABS}"
+        assert num / den <= BF16_O_RELFRO, f"{label}: O rel-Frobenius {num / den:.3e} > {BF16_O_RELFRO}"
+        assert err_l <= BF16_LSE_ABS, f"{label}: LSE max-abs {err_l:.3e} > {BF16_LSE_ABS}"
+    return err_o, err_l

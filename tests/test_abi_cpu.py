@@ -1,0 +1,126 @@
+"""CPU-only checks of the C ABI: the library loads, exports every declared symbol, and rejects
+bad arguments on the host before anything is launched (no GPU is touched)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ra.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ra_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def ra():
+    import striped_blockwise_amd as m
+    try:
+        m.lib()
+    except m.RaError as e:
+        pytest.fail(f"libra.so is not built: {e}")
+    return m
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for want in ("ra_abi_version", "ra_last_error", "ra_check", "ra_tile_shape", "ra_permute",
+                 "ra_permute_ids", "ra_round", "ra_merge", "ra_forward"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(ra):
+    L = ra.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+        assert isinstance(getattr(L, name), ctypes._CFuncPtr)
+
+
+def test_abi_version_and_tiles(ra):
+    assert ra.abi_version() == 1
+    tq, tk = ra.tile_shape(ra.BF16, 128)
+    assert tq > 0 and tk > 0 and tq % 32 == 0 and tk % 16 == 0
+    assert ra.tile_shape(ra.F32, 64)[0] > 0
+    with pytest.raises(NotImplementedError):
+        ra.tile_shape(ra.BF16, 64)
+    with pytest.raises(ValueError):
+        ra.tile_shape(7, 128)
+
+
+@pytest.mark.parametrize("kw,exc,msg", [
+    (dict(n=10, P=4), ValueError, "multiple of P"),
+    (dict(P=0), ValueError, "P must be"),
+    (dict(p=4), ValueError, "p=4"),
+    (dict(kv=-1), ValueError, "kv=-1"),
+    (dict(d=96), NotImplementedError, "head dim 96"),
+    (dict(d=0), ValueError, "head dim d"),
+    (dict(dtype=5), ValueError, "dtype"),
+    (dict(layout=2), ValueError, "layout"),
+    (dict(scale=float("nan")), ValueError, "scale"),
+    (dict(B=-1), ValueError, ">= 0"),
+    (dict(n=1 << 40, P=1), ValueError, "too large"),
+])
+def test_check_rejects(ra, kw, exc, msg):
+    args = dict(B=1, H=8, n=8192, d=128, P=4, dtype=ra.BF16, layout=ra.STRIPED, causal=True,
+                scale=0.0, p=0, kv=0)
+    args.update(kw)
+    with pytest.raises(exc, match=re.escape(msg)):
+        ra.check(**args)
+
+
+def test_check_accepts_every_workload(ra):
+    import workloads
+    for w in workloads.WORKLOADS.values():
+        dt = ra.F32 if w.dtype == "f32" else ra.BF16
+        for layout in (ra.CONTIGUOUS, ra.STRIPED):
+            ra.check(w.B, w.H, w.n, w.d, w.P, dt, layout, True, 0.0, p=w.P - 1, kv=0)
+    ra.check(0, 8, 0, 128, 4)            # empty problems are valid
+
+
+def test_raw_abi_rejects_null_and_bad_sizes_without_gpu(ra):
+    L = ra.lib()
+    assert L.ra_permute(None, None, 1, 16, 256, 4, 0, None) == -1
+    assert b"NULL" in L.ra_last_error()
+    assert L.ra_permute(None, None, 1, 18, 256, 4, 0, None) == -1       # n % P
+    assert L.ra_permute(None, None, 1, 16, 6, 4, 0, None) == -1         # row_bytes % 4
+    assert L.ra_permute(None, None, 0, 16, 256, 4, 0, None) == 0        # empty: no-op
+    assert L.ra_last_error() == b""
+    assert L.ra_merge(None, None, None, None, 0, 128, None) == 0        # empty: no-op
+    assert L.ra_merge(None, None, None, None, 4, 128, None) == -1
+    pr = ra._problem(1, 1, 256, 64, 4, ra.F32, ra.CONTIGUOUS, True, 0.0)
+    assert L.ra_round(ctypes.byref(pr), None, None, None, 0, 0, 0, 0, None, None, None, None) == -1
+    assert L.ra_forward(ctypes.byref(pr), None, None, None, 0, 4, None, ra.F32, None, None, None) == -1
+    assert L.ra_forward(ctypes.byref(pr), None, None, None, 2, 1, None, ra.F32, None, None, None) == -1
+    assert b"device range" in L.ra_last_error()
+    empty = ra._problem(1, 1, 0, 64, 4, ra.F32, ra.CONTIGUOUS, True, 0.0)
+    assert L.ra_forward(ctypes.byref(empty), None, None, None, 0, 4, None, ra.F32, None, None, None) == 0
+    bad = ra._problem(1, 1, 256, 64, 4, ra.F32, ra.CONTIGUOUS, True, 0.0)
+    bad.causal = 2
+    assert L.ra_check(ctypes.byref(bad), 0, 0) == -1 and b"causal" in L.ra_last_error()
+    # misaligned pointer (never dereferenced: validation fails first)
+    assert L.ra_permute(ctypes.c_void_p(2), ctypes.c_void_p(4096), 1, 16, 8, 4, 0, None) == -1
+
+
+def test_binding_refuses_cpu_tensors(ra):
+    x = torch.zeros((1, 1, 64, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        ra.forward(x, x, x, 4)
+    with pytest.raises(ValueError, match="GPU"):
+        ra.permute(x, 4)
+
+
+def test_product_package_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "striped_blockwise_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), f
+                assert "oracle/" not in text and "import workloads" not in text, f
