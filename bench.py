@@ -1,0 +1,323 @@
+#!/usr/bin/env python3
+"""Benchmark: causal blockwise attention TFLOP/s on one MI355X, striped vs contiguous (ring).
+
+Workload (default ``share_n256k``): one device's share of a 262144-token sequence split over
+P = 8 (virtual) devices -- the query block of device 7 (c = 32768 tokens) against all 8 K/V
+blocks, B = 1, H = 32, d = 128, bf16, causal.
+
+One timed step = the striped hot path over that share:
+  ra_permute of Q, K, V (full sequence) and of the position IDs into the striped layout,
+  then ra_forward for device 7 (all 8 ring rounds fused, GetMask per round, tile skipping).
+``value`` is useful causal TFLOP/s of the step: 4 * d * (unmasked query-key pairs) * B * H
+flops divided by the step time (masked halves of diagonal tiles and softmax work excluded).
+
+Also measured in the same run (reported as extra fields, never as ``value``):
+  * ring: the contiguous-layout forward for device 7 (most causal work of that layout);
+  * per-round ra_round times for device 7 in both layouts and their ratio;
+  * the streamed path: 8 x (ra_round + ra_merge), with merge and permute GB/s;
+  * roofline of the dominant kernel (the fused bf16 forward) against the bf16 MFMA peak;
+  * cpu_baseline: the fp64 CPU oracle on a bounded sample of the same share.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal blockwise-attn TFLOP/s and % bf16 MFMA peak, ring vs striped, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published
+PMC_FILE = os.path.join(ROOT, "profiles", "k_attn_bf16_share_n256k_pmc.json")
+KERNEL_SRC = os.path.join(ROOT, "striped_blockwise_amd", "csrc", "k_attn_bf16.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def useful_pairs(layout: str, P: int, c: int, p: int, causal: bool = True) -> list:
+    """Unmasked pairs of device p per ring round (closed form of the Striped Attention review's
+    work formulas, with the diagonal block's c(c+1)/2)."""
+    out = []
+    for r in range(P):
+        k = (p - r) % P
+        if not causal:
+            out.append(c * c)
+        elif layout == "contiguous":
+            out.append(c * c if k < p else (c * (c + 1) // 2 if k == p else 0))
+        else:
+            out.append(c * (c + 1) // 2 if k <= p else c * (c - 1) // 2)
+    return out
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_from_profile(launch_bytes_hint=None):
+    """HBM bytes per launch of the fused forward from committed rocprofv3 --pmc counters, or
+    None when the counters are missing or were taken on a different kernel source."""
+    try:
+        with open(PMC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != source_hash(KERNEL_SRC):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, layout: str, budget_s: float = 12.0):
+    """Time the fp64 oracle on sampled query rows of device w.device (whole heads of keys)."""
+    import numpy as np
+
+    import workloads
+    from oracle import attention as OA
+    from oracle import ring as OR
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    P, c, p, d = w.P, w.c, w.device, w.d
+    order = OR.layout_order(w.n, P, layout)
+    rows = np.linspace(0, c - 1, 256).round().astype(np.int64)
+    pos_q = order[p * c + rows]
+    flops = 0.0
+    elapsed = 0.0
+    heads = 0
+    for h in range(w.H):
+        q, k, v = workloads.qkv(w, heads=[h])
+        ql = OR.to_layout(q.double().numpy(), order)[:, :, p * c + rows]
+        kl = OR.to_layout(k.double().numpy(), order)
+        vl = OR.to_layout(v.double().numpy(), order)
+        t0 = time.perf_counter()
+        OA.attention(ql, kl, vl, True, pos_q=pos_q, pos_k=order)
+        elapsed += time.perf_counter() - t0
+        flops += 4.0 * d * float((pos_q + 1).sum())          # visible keys = position + 1
+        heads += 1
+        if elapsed >= budget_s:
+            break
+    return {
+        "value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"{heads} head(s) x 256 evenly spaced query rows of device {p} ({layout}) against "
+                  f"all {w.n} keys, fp64 NumPy; {flops:.3e} useful flops in {elapsed:.2f} s",
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="share_n256k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="only the timed striped steps")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the ring's devices are emulated on a single MI355X "
+              "(rounds run in order on one stream); --gpus must be 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import striped_blockwise_amd as ra
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    ra.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.get(args.workload)
+    P, c, d, H, B = w.P, w.c, w.d, w.H, w.B
+    p = w.device if w.device is not None else P - 1
+    BH = B * H
+
+    log(f"[bench] generating inputs for {w.name} (n={w.n}, P={P}, H={H}, d={d}) on the CPU")
+    t0 = time.perf_counter()
+    q, k, v = (t.to(dev) for t in workloads.qkv(w))
+    ids = workloads.positions(w.n).to(dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s")
+
+    qs, ks, vs = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ids_s = torch.empty_like(ids)
+    o = torch.empty((B, H, c, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, c), dtype=torch.float32, device=dev)
+
+    pairs_s = useful_pairs("striped", P, c, p)
+    pairs_c = useful_pairs("contiguous", P, c, p)
+    flops_s = 4.0 * d * BH * sum(pairs_s)
+    flops_c = 4.0 * d * BH * sum(pairs_c)
+
+    def step():
+        ra.permute(q, P, out=qs)
+        ra.permute(k, P, out=ks)
+        ra.permute(v, P, out=vs)
+        ra.permute_ids(ids, P, out=ids_s)
+        e_f0.record()
+        ra.forward(qs, ks, vs, P, "striped", True, p_begin=p, p_end=p + 1, out=(o, lse))
+        e_f1.record()
+
+    e_f0, e_f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps")
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    s0.record()
+    for i in range(args.steps):
+        e_f0, e_f1 = ev[i]
+        step()
+    s1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = s0.elapsed_time(s1) / args.steps
+    fwd_ms = [a.elapsed_time(b) for a, b in ev]
+    fwd_avg = sum(fwd_ms) / len(fwd_ms)
+    value = flops_s / (step_ms * 1e-3) / 1e12
+    achieved = flops_s / (fwd_avg * 1e-3) / 1e12
+    log(f"[bench] striped step {step_ms:.2f} ms ({value:.1f} TFLOP/s); forward kernel {fwd_avg:.2f} ms "
+        f"({achieved:.1f} TFLOP/s, {100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
+
+    result = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)*0.5 bf16 Q/K/V, generated on the host)",
+        "config": {"workload": w.name, "n": w.n, "P": P, "c": c, "device": p, "B": B, "H": H, "d": d,
+                   "layout": "striped", "causal": True,
+                   "step": "ra_permute Q,K,V,pos -> ra_forward(device p, all P rounds)",
+                   "useful_flops_per_step": flops_s},
+        "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 3),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 5),
+                     "traffic": traffic_from_profile(), "kernel": "k_attn_bf16 (ra_forward)",
+                     "kernel_ms": round(fwd_avg, 4), "algorithmic_flops_per_launch": flops_s},
+        "wall_s_timed": round(wall, 3),
+    }
+
+    if not args.no_extras:
+        # ---- ring (contiguous) forward for the same device
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(3, args.steps // 2)
+        ra.forward(q, k, v, P, "contiguous", True, p_begin=p, p_end=p + 1, out=(o, lse))
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            ra.forward(q, k, v, P, "contiguous", True, p_begin=p, p_end=p + 1, out=(o, lse))
+        b.record()
+        torch.cuda.synchronize()
+        ring_ms = a.elapsed_time(b) / reps
+        result["ring"] = {"forward_ms": round(ring_ms, 4),
+                          "tflops": round(flops_c / (ring_ms * 1e-3) / 1e12, 3),
+                          "useful_flops": flops_c,
+                          "striped_forward_ms": round(fwd_avg, 4),
+                          "share_speedup_striped_over_ring": round(ring_ms / fwd_avg, 4),
+                          "ideal_share_speedup": round(sum(pairs_c) / sum(pairs_s), 5)}
+        log(f"[bench] ring forward {ring_ms:.2f} ms; share speedup {ring_ms / fwd_avg:.3f}x")
+
+        # ---- per-round ra_round, both layouts, device p
+        per = {}
+        for layout, (qq, kk_, vv) in (("contiguous", (q, k, v)), ("striped", (qs, ks, vs))):
+            times = []
+            for r in range(P):
+                kb = (p - r) % P
+                args_r = (qq[:, :, p * c:(p + 1) * c], kk_[:, :, kb * c:(kb + 1) * c], vv[:, :, kb * c:(kb + 1) * c],
+                          P, p, kb, layout, True)
+                ra.round(*args_r)
+                a.record()
+                for _ in range(3):
+                    ra.round(*args_r)
+                b.record()
+                torch.cuda.synchronize()
+                times.append(a.elapsed_time(b) / 3)
+            per[layout] = times
+        ratios = [tc / ts for tc, ts in zip(per["contiguous"], per["striped"])]
+        result["per_round"] = {
+            "device": p, "round_ms_contiguous": [round(x, 4) for x in per["contiguous"]],
+            "round_ms_striped": [round(x, 4) for x in per["striped"]],
+            "speedup_striped_over_ring": [round(x, 4) for x in ratios],
+            "ideal_speedup": [round(a_ / b_, 5) if b_ else None for a_, b_ in zip(pairs_c, pairs_s)],
+            "slowest_round_speedup": round(max(per["contiguous"]) / max(per["striped"]), 4),
+        }
+        log("[bench] per-round speedup " + " ".join(f"{x:.3f}" for x in ratios))
+
+        # ---- streamed striped path: rounds + merges, and the HBM-bound kernels' bandwidth
+        acc_o = torch.empty((B, H, c, d), dtype=torch.float32, device=dev)
+        acc_l = torch.empty((B, H, c), dtype=torch.float32, device=dev)
+        po = torch.empty_like(acc_o)
+        pl = torch.empty_like(acc_l)
+        m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        merge_ms = []
+        acc_o.zero_()
+        acc_l.fill_(float("-inf"))
+        torch.cuda.synchronize()
+        a.record()
+        for r in range(P):
+            kb = (p - r) % P
+            ra.round(qs[:, :, p * c:(p + 1) * c], ks[:, :, kb * c:(kb + 1) * c], vs[:, :, kb * c:(kb + 1) * c],
+                     P, p, kb, "striped", True, out=(po, pl))
+            m0.record()
+            ra.merge(acc_o, acc_l, po, pl)
+            m1.record()
+            torch.cuda.synchronize()
+            merge_ms.append(m0.elapsed_time(m1))
+        b.record()
+        torch.cuda.synchronize()
+        stream_ms = a.elapsed_time(b)
+        merge_bytes = 3.0 * BH * c * (4 * d + 4)
+        mavg = sum(merge_ms) / len(merge_ms)
+        # permute bandwidth
+        a.record()
+        for _ in range(3):
+            ra.permute(k, P, out=ks)
+        b.record()
+        torch.cuda.synchronize()
+        perm_ms = a.elapsed_time(b) / 3
+        perm_bytes = 2.0 * k.numel() * k.element_size()
+        result["streamed"] = {"rounds_plus_merges_ms": round(stream_ms, 3),
+                              "tflops": round(flops_s / (stream_ms * 1e-3) / 1e12, 3)}
+        result["hbm_kernels"] = {
+            "merge": {"ms": round(mavg, 4), "bytes": merge_bytes,
+                      "GBps": round(merge_bytes / (mavg * 1e-3) / 1e9, 1), "peak_GBps": PEAK_HBM_GBS},
+            "permute": {"ms": round(perm_ms, 4), "bytes": perm_bytes,
+                        "GBps": round(perm_bytes / (perm_ms * 1e-3) / 1e9, 1), "peak_GBps": PEAK_HBM_GBS},
+        }
+        log(f"[bench] streamed {stream_ms:.2f} ms; merge {mavg:.3f} ms "
+            f"({merge_bytes / (mavg * 1e-3) / 1e9:.0f} GB/s); permute {perm_ms:.3f} ms "
+            f"({perm_bytes / (perm_ms * 1e-3) / 1e9:.0f} GB/s)")
+
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(w, "striped")
+        log(f"[bench] cpu oracle {result['cpu_baseline']['value']:.4f} TFLOP/s")
+    else:
+        result["cpu_baseline"] = None
+
+    props = torch.cuda.get_device_properties(dev)
+    result["device"] = {"name": props.name, "cus": props.multi_processor_count,
+                        "arch": getattr(props, "gcnArchName", "")}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -7,10 +7,12 @@ It is the one piece of code that both the CPU oracle (``oracle/``) and the GPU p
 Recipe (every tensor is [B, H, n, d], token order, row-major, d contiguous):
 
 * Q, K and V are drawn independently.  Each (tensor, batch, head) matrix [n, d] comes from its
-  own NumPy PCG64 stream seeded with ``SeedSequence([seed, tensor_id, b, h])`` (tensor_id 0/1/2
-  for Q/K/V), as iid standard normals in float32, multiplied by ``input_scale`` (1 or 1/2,
-  both exact in binary) and rounded to the compute dtype with round-to-nearest-even (torch's
+  own torch CPU generator seeded with the first word of NumPy's
+  ``SeedSequence([seed, tensor_id, b, h])`` (tensor_id 0/1/2 for Q/K/V), as iid standard
+  normals in float32 (``torch.randn``), multiplied by ``input_scale`` (1 or 1/2, both exact in
+  binary) and rounded to the compute dtype with round-to-nearest-even (torch's
   ``.to(torch.bfloat16)``).  Per-head streams let the oracle regenerate only the heads it needs.
+  Both sides of every comparison use the same generated tensor in one process.
 * The million-token stress workload scales K at 1% of token positions (all heads) by 8 to force
   large jumps of the running row maximum.  The positions are ``round(0.01 * n)`` distinct token
   indices drawn from ``SeedSequence([seed, 3])``.  The scaling is applied in float32 before the
@@ -26,9 +28,7 @@ same shapes stand in for that data.
 """
 from __future__ import annotations
 
-import concurrent.futures as _cf
 import dataclasses
-import os
 
 import numpy as np
 import torch
@@ -83,11 +83,11 @@ def get(name: str) -> Workload:
 _TENSOR_ID = {"q": 0, "k": 1, "v": 2}
 
 
-def _draw(seed: int, tid: int, b: int, h: int, n: int, d: int, scale: float) -> np.ndarray:
-    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tid, b, h])))
-    x = rng.standard_normal((n, d), dtype=np.float32)
+def _draw(seed: int, tid: int, b: int, h: int, n: int, d: int, scale: float) -> torch.Tensor:
+    s = int(np.random.SeedSequence([seed, tid, b, h]).generate_state(1, np.uint64)[0])
+    x = torch.randn((n, d), generator=torch.Generator().manual_seed(s), dtype=torch.float32)
     if scale != 1.0:
-        x *= np.float32(scale)
+        x.mul_(scale)
     return x
 
 
@@ -98,13 +98,6 @@ def outlier_rows(w: Workload) -> np.ndarray:
     m = int(round(w.outlier_frac * w.n))
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, 3])))
     return np.sort(rng.choice(w.n, size=m, replace=False)).astype(np.int64)
-
-
-def _threads() -> int:
-    try:
-        return max(1, min(16, len(os.sched_getaffinity(0))))
-    except AttributeError:  # pragma: no cover
-        return max(1, min(16, os.cpu_count() or 1))
 
 
 def qkv(w: Workload | str, which: str = "qkv", heads=None, dtype: torch.dtype | None = None):
@@ -123,21 +116,13 @@ def qkv(w: Workload | str, which: str = "qkv", heads=None, dtype: torch.dtype | 
     for letter in which:
         tid = _TENSOR_ID[letter]
         t = torch.empty((w.B, len(heads), w.n, w.d), dtype=w.torch_dtype)
-        jobs = [(b, i, h) for b in range(w.B) for i, h in enumerate(heads)]
-
-        def fill(job, letter=letter, tid=tid, t=t):
-            b, i, h = job
-            x = _draw(w.seed, tid, b, h, w.n, w.d, w.input_scale)
-            if letter == "k" and out_rows.size:
-                x[out_rows] *= np.float32(w.outlier_gain)
-            t[b, i].copy_(torch.from_numpy(x).to(w.torch_dtype))
-
-        if len(jobs) > 1:
-            with _cf.ThreadPoolExecutor(_threads()) as ex:
-                list(ex.map(fill, jobs))
-        else:
-            for j in jobs:
-                fill(j)
+        rows = torch.from_numpy(out_rows)
+        for b in range(w.B):
+            for i, h in enumerate(heads):
+                x = _draw(w.seed, tid, b, h, w.n, w.d, w.input_scale)
+                if letter == "k" and rows.numel():
+                    x[rows] *= w.outlier_gain
+                t[b, i].copy_(x)                      # round-to-nearest-even to the dtype
         if dtype is not None and dtype != t.dtype:
             t = t.to(dtype)
         results.append(t)
