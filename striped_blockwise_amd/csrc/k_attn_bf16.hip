@@ -7,17 +7,24 @@
 // per tile: a tile with no visible pair is skipped ("分块与分瓦片"), a tile with every pair
 // visible runs unmasked, and only tiles that straddle the diagonal pay for an element mask.
 //
-// Data flow per 64-key tile:
-//   HBM --(16 B per lane, coalesced)--> registers --> LDS (K row-major, V transposed), double
-//   buffered so the next tile's global loads are in flight while this tile computes.
-//   S^T = K Q^T on MFMA: A = K rows from LDS, B = the wave's Q columns held in registers.
-//   In this orientation each lane owns one query column, so row max / row sum are in-lane
+// Data flow per TK-key tile:
+//   HBM -> LDS by DMA (buffer_load ... lds, 16 B per lane), K and V both row-major with a
+//   16-byte-chunk XOR swizzle; no registers or VALU work on the way in.  K and V each have two
+//   LDS stages; the loads for tile t+2 (K) and t+1 (V) are in flight while tile t computes.
+//   S^T = K Q^T on MFMA: A = 32 K rows from LDS, B = the wavefront's Q columns in registers.
+//   In this orientation each lane owns one query, so the row max / row sum are in-lane
 //   reductions plus one v_permlane32_swap with the other half of the wavefront.
 //   P = exp2(S * scale * log2e - m) in fp32, rounded to bf16 (round-to-nearest-even).
-//   O^T += V^T P^T on MFMA: A = V^T from LDS, B = P straight from the score registers (the MFMA
-//   contraction index is permuted consistently on both operands, so no register shuffles).
-// The output accumulator O^T keeps one query per lane too, so the online-softmax rescale is a
-// per-lane multiply.
+//   O^T += V^T P^T on MFMA: A = V^T, read from the row-major V tile with ds_read_b64_tr_b16
+//   (which transposes 4x4 blocks of 16-bit elements across lanes), B = P straight from the
+//   score registers (the contraction index is permuted identically on both operands).
+//   Software pipelining: the S MFMAs of tile t+1 are issued in the same basic block as the
+//   softmax VALU work of tile t, so the matrix cores and the vector ALUs overlap.
+// The running max is only raised when a tile's max exceeds it by more than 2^8 (in exp2
+// units), so the rescale of O (64-128 multiplies per lane) is rare; the result is exact either
+// way because O, l and the reference max always stay consistent.
+#include <type_traits>
+
 #include "ra_internal.h"
 
 namespace ra {
@@ -25,107 +32,144 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int D = 128;          // head dim
-constexpr int TK = 64;          // keys per tile
+constexpr int ROWB = D * 2;     // bytes per K / V row
 constexpr int NW = 4;           // wavefronts per workgroup
 constexpr int NT = NW * 64;     // threads per workgroup
-constexpr int KS_BYTES = TK * D * 2;       // K tile in LDS
-constexpr int VS_BYTES = TK * D * 2;       // V^T tile in LDS
-constexpr int STAGE_BYTES = KS_BYTES + VS_BYTES;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
+constexpr float TAU = 8.0f;     // lazy-rescale threshold, log2 units
 
-static_assert(NT == 256, "loader mapping assumes 256 threads");
+#ifndef RA_BF16_QB
+#define RA_BF16_QB 1            // 32-query column blocks per wavefront
+#endif
+#ifndef RA_BF16_TK
+#define RA_BF16_TK 32           // keys per tile
+#endif
+#ifndef RA_BF16_PIPE
+#define RA_BF16_PIPE 0          // 1: S of tile t+1 overlaps the softmax of tile t
+#endif
+#ifndef RA_BF16_DOT2SUM
+#define RA_BF16_DOT2SUM 0       // 1: row sums with v_dot2 on the rounded probabilities
+#endif
+#ifndef RA_BF16_OCC
+#define RA_BF16_OCC 2           // target wavefronts per SIMD
+#endif
 
-// ---- LDS layouts ------------------------------------------------------------------------------
-// K tile: row = key (0..63), 256 B per row = 16 chunks of 16 B; chunk index XOR (row & 15) so
-// that the 32 rows one MFMA operand read touches spread over all banks.
-__device__ inline int k_off(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
-
-// V^T tile: row = head-dim index d (0..127), 64 keys x 2 B = 128 B per row = 8 chunks of 16 B.
-// Keys are stored in MFMA-operand order: inside each group of 16 keys the order is
-// [0-3, 8-11, 4-7, 12-15], so lane half h reads its 8 keys {4h..4h+3, 8+4h..8+4h+3} as one
-// 16-byte chunk.  Chunk index XOR a hash of d keeps both the operand reads (32 consecutive d)
-// and the transposing writes (d spaced by 8) spread over the banks.
-__device__ inline int vt_swz(int d) { return (d & 7) ^ ((d >> 3) & 7); }
-__device__ inline int vt_off(int d, int chunk8, int within_bytes) {
-  return d * 128 + ((chunk8 ^ vt_swz(d)) << 4) + within_bytes;
+// LDS layout of a K or V tile: row = key, 256 B = 16 chunks of 16 B, each row's chunks permuted
+// by an XOR with a per-row mask.  K tiles are read as MFMA A operands (32 consecutive rows, one
+// chunk): mask = row & 15 puts any 16 consecutive rows on 16 different chunks.  V tiles are read
+// with ds_read_b64_tr_b16, where one 32-lane half reads 4 consecutive rows x 4 consecutive
+// chunks (8 B per lane): mask bits {0b1010 for row bit 0, 0b0100 for row bit 1} make those 16
+// (row, chunk) pairs land on 16 different chunks, and any 16 lanes on 8 different chunk pairs.
+__device__ __forceinline__ int k_swz(int row) { return row & 15; }
+__device__ __forceinline__ int v_swz(int row) { return ((row & 1) ? 10 : 0) ^ ((row & 2) ? 4 : 0); }
+__device__ __forceinline__ int k_off(int row, int byte_in_row) {
+  return row * ROWB + ((((byte_in_row >> 4) ^ k_swz(row))) << 4) + (byte_in_row & 15);
+}
+__device__ __forceinline__ int v_off(int row, int byte_in_row) {
+  return row * ROWB + ((((byte_in_row >> 4) ^ v_swz(row))) << 4) + (byte_in_row & 15);
 }
 
-struct KVRegs {
-  u32x4 k[4];
-  u32x4 v[4];
-};
-
-// Global -> registers for tile starting at key x0.  Thread t loads K rows x0 + t/16 + 16 i
-// (16-byte chunk t % 16) and V rows x0 + 4 (t/16) + i (same chunk): 256 threads x 4 x 16 B per
-// tensor.  Rows at or past c read as zeros.
-__device__ inline void load_tile(KVRegs& R, const __bf16* kp, const __bf16* vp, int x0, int c,
-                                 int tid) {
-  const int ch = tid & 15;
-  const int g = tid >> 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rk = x0 + g + 16 * i;
-    const int rv = x0 + 4 * g + i;
-    R.k[i] = rk < c ? *reinterpret_cast<const u32x4*>(kp + (int64_t)rk * D + ch * 8) : u32x4{0, 0, 0, 0};
-    R.v[i] = rv < c ? *reinterpret_cast<const u32x4*>(vp + (int64_t)rv * D + ch * 8) : u32x4{0, 0, 0, 0};
-  }
-}
-
-// Registers -> LDS stage.  K rows go straight in; V is transposed: each thread holds the same
-// 8 head-dim values of 4 consecutive keys and writes, per head-dim index, those 4 keys (8 B).
-__device__ inline void store_tile(char* stage, const KVRegs& R, int tid) {
-  char* ks = stage;
-  char* vs = stage + KS_BYTES;
-  const int ch = tid & 15;
-  const int g = tid >> 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = g + 16 * i;
-    *reinterpret_cast<u32x4*>(ks + k_off(row, ch)) = R.k[i];
-  }
-  // keys 4g..4g+3 -> operand order position: group g/4 of 16, quad q = g % 4
-  const int quad = g & 3;
-  const int chunk8 = 2 * (g >> 2) + (quad & 1);
-  const int within = (quad >> 1) * 8;     // bytes: 4 keys x 2 B
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {           // dword j of the chunk = head-dim pair (2j, 2j+1)
-    const uint32_t a0 = R.v[0][j], a1 = R.v[1][j], a2 = R.v[2][j], a3 = R.v[3][j];
-    const u32x2 lo = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-    const u32x2 hi = {(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-    const int d0 = ch * 8 + 2 * j;
-    *reinterpret_cast<u32x2*>(vs + vt_off(d0, chunk8, within)) = lo;
-    *reinterpret_cast<u32x2*>(vs + vt_off(d0 + 1, chunk8, within)) = hi;
-  }
-}
-
-__device__ inline float pair_max(float x) {
+__device__ __forceinline__ float pair_max(float x) {
   const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
-__device__ inline float pair_sum(float x) {
+__device__ __forceinline__ float pair_sum(float x) {
   const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-// Key index (within the 32-key MFMA block) held by accumulator register r in lane half h.
-__device__ inline int acc_row(int r, int h) { return (r >> 2) * 8 + h * 4 + (r & 3); }
+// Key index (within a 32-key MFMA block) held by accumulator register r in lane half h.
+__device__ __forceinline__ int acc_row(int r, int h) { return (r >> 2) * 8 + h * 4 + (r & 3); }
 
-template <int QB, bool STATS>
-__global__ __launch_bounds__(NT, (QB == 1 ? 2 : 1)) void k_attn_bf16(AttnArgs a) {
-  constexpr int QW = 32 * QB;            // query rows per wavefront
-  constexpr int TQ = NW * QW;            // query rows per workgroup
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE_BYTES];
+template <int QB, int TK, bool STATS>
+struct Attn {
+  static constexpr int QW = 32 * QB;              // query rows per wavefront
+  static constexpr int TQ = NW * QW;              // query rows per workgroup
+  static constexpr int KB = TK / 32;              // 32-key MFMA blocks per tile
+  static constexpr int KS = TK / 16;              // 16-key MFMA k-steps per tile (P V)
+  static constexpr int TILE = TK * ROWB;          // bytes of one K or V tile
+  static constexpr int DMA_PER_WAVE = TILE / (NW * 1024);   // 1 KB per wave-wide DMA
+
+  // Per-lane constant parts of the LDS addresses.
+  int k_base[8];       // K operand: row l32, chunk (2 dk + hh)
+  int v_base[4][2];    // V^T operand: transposed reads, [d-block][first/second 4 keys]
+
+  __device__ __forceinline__ void init_offsets(int lane) {
+    const int l32 = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int dk = 0; dk < 8; ++dk) k_base[dk] = k_off(l32, (2 * dk + hh) * 16);
+    // ds_read_b64_tr_b16: in each 16-lane group, result lane 4a+b element e comes from element b
+    // of source lane 4e+a.  Source lane (G, e, a) therefore points at V[key(G, e)][d(G, a)..+3]
+    // with key = 4 h + e (+8 for the second read), h = G / 2, and d = 16 (G % 2) + 4 a, so that
+    // result lane L holds d = 32 db + L % 32 and keys {4h..4h+3} / {8+4h..8+4h+3}.
+    const int G = lane >> 4, e = (lane >> 2) & 3, aa = lane & 3;
+    const int h = G >> 1, g2 = G & 1;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int sec = 0; sec < 2; ++sec) {
+        const int key = 4 * h + e + 8 * sec;
+        const int d = 32 * db + 16 * g2 + 4 * aa;
+        v_base[db][sec] = v_off(key, 2 * d);
+      }
+  }
+};
+
+// DMA one K or V tile (keys x0 .. x0+TK-1 of a block of c rows at `block`) into an LDS stage.
+// The buffer descriptor starts at row x0 and holds only the rows that exist, so the per-lane
+// offsets are loop constants and rows past the end of the block are out of range: the buffer
+// unit returns zeros for them, which land in LDS (zero keys are masked out of the scores, and
+// zero values contribute nothing).
+template <int DMA_PER_WAVE>
+__device__ __forceinline__ void dma_tile(const char* block, char* stage, int x0, int c,
+                                         const unsigned* voff, int wave_u) {
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(block + (int64_t)x0 * ROWB), 0, (c - x0) * ROWB, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < DMA_PER_WAVE; ++i) {
+    const int seg = wave_u * DMA_PER_WAVE + i;            // 1 KB segment = 4 rows
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(stage + seg * 1024), 16, voff[i], 0, 0, 0);
+  }
+}
+
+// Per-lane byte offsets (relative to the tile's first row) of a wave's DMA segments: lane j of
+// segment seg fills LDS row 4 seg + j / 16 at physical chunk j % 16, which holds logical chunk
+// (j % 16) ^ mask(row) of that row (the XOR permutation is its own inverse).
+template <int DMA_PER_WAVE, bool IS_V>
+__device__ __forceinline__ void dma_offsets(unsigned* voff, int wave_u, int lane) {
+#pragma unroll
+  for (int i = 0; i < DMA_PER_WAVE; ++i) {
+    const int row = (wave_u * DMA_PER_WAVE + i) * 4 + (lane >> 4);
+    const int mask = IS_V ? v_swz(row) : k_swz(row);
+    voff[i] = (unsigned)(row * ROWB + (((lane & 15) ^ mask) << 4));
+  }
+}
+
+__device__ __forceinline__ void wait_dma_and_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's LDS DMA has landed
+  __syncthreads();
+}
+
+template <int QB, int TK, bool STATS>
+__global__ __launch_bounds__(NT, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) {
+  using A = Attn<QB, TK, STATS>;
+  constexpr int QW = A::QW, TQ = A::TQ, KB = A::KB, KS = A::KS, TILE = A::TILE;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];   // K0 K1 V0 V1
+  auto kst = [&](int i) __attribute__((always_inline)) { return smem + (i & 1) * TILE; };
+  auto vst = [&](int i) __attribute__((always_inline)) { return smem + (2 + (i & 1)) * TILE; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const int c = a.c;
@@ -138,22 +182,26 @@ __global__ __launch_bounds__(NT, (QB == 1 ? 2 : 1)) void k_attn_bf16(AttnArgs a)
   const int p = a.p_begin + dev;
   const int q_wg0 = qt * TQ;
   const int q_wg_last = min(c, q_wg0 + TQ) - 1;
-  const int qw0 = q_wg0 + wave * QW;
+  const int qw0 = q_wg0 + wave_u * QW;
   const int qw_last = min(c, qw0 + QW) - 1;  // < qw0 when the wave has no rows
   const bool wave_live = qw0 < c;
 
-  // ---- Q columns for the B operand: lane holds row qw0 + 32 qb + l32, head-dim chunk
-  //      16 dk + 8 hh .. +7 for every dk.
+  A off;
+  off.init_offsets(lane);
+  unsigned dko[A::DMA_PER_WAVE], dvo[A::DMA_PER_WAVE];
+  dma_offsets<A::DMA_PER_WAVE, false>(dko, wave_u, lane);
+  dma_offsets<A::DMA_PER_WAVE, true>(dvo, wave_u, lane);
+
+  // ---- Q columns (B operand): lane holds row qw0 + 32 qb + l32, head dims 16 dk + 8 hh .. +7
   const __bf16* qp = (const __bf16*)a.q + bh * a.q_bh_stride + dev * a.q_dev_stride;
   bf16x8 qf[QB][8];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = qw0 + qb * 32 + l32;
 #pragma unroll
-    for (int dk = 0; dk < 8; ++dk) {
+    for (int dk = 0; dk < 8; ++dk)
       qf[qb][dk] = row < c ? *reinterpret_cast<const bf16x8*>(qp + (int64_t)row * D + dk * 16 + hh * 8)
                            : bf16x8{};
-    }
   }
 
   f32x16 o[QB][4];
@@ -165,6 +213,106 @@ __global__ __launch_bounds__(NT, (QB == 1 ? 2 : 1)) void k_attn_bf16(AttnArgs a)
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) { m[qb] = -INFINITY; l[qb] = 0.f; }
   const float cs = a.scale * LOG2E;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  // S^T tile of one wavefront: [qb][32-key block]
+  f32x16 sA[QB][KB];
+#if RA_BF16_PIPE
+  f32x16 sB[QB][KB];
+#endif
+
+  // S^T = K Q^T for one tile.  All K fragments of a 32-key block are requested from LDS before
+  // the first MFMA that needs one (the scheduling barrier keeps the compiler from interleaving
+  // each read with its MFMA), so the LDS latency is paid once per block, not once per MFMA.
+  auto compute_s = [&](const char* ks_, f32x16 (&s)[QB][KB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      bf16x8 kf[8];
+#pragma unroll
+      for (int dk = 0; dk < 8; ++dk)
+        kf[dk] = *reinterpret_cast<const bf16x8*>(ks_ + off.k_base[dk] + kb * 32 * ROWB);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[qb][kb] = f32x16{};
+#pragma unroll
+      for (int dk = 0; dk < 8; ++dk)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[dk], qf[qb][dk], s[qb][kb], 0, 0, 0);
+    }
+  };
+
+  // softmax of tile s (scores already masked) -> P (bf16, B-operand order), updates m, l, o
+  auto softmax_pv = [&](f32x16 (&s)[QB][KB], const char* vs_) __attribute__((always_inline)) {
+    // row max and lazy rescale
+    float ref[QB];
+    bool any_grow = false;
+    float mt[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = s[qb][0][0];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int rg = 0; rg < 16; ++rg) mx = fmaxf(mx, s[qb][kb][rg]);
+      mt[qb] = pair_max(mx) * cs;
+      any_grow |= mt[qb] > m[qb] + TAU;
+    }
+    if (__builtin_amdgcn_ballot_w64(any_grow)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const bool grow = mt[qb] > m[qb] + TAU;
+        const float m_new = grow ? mt[qb] : m[qb];
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m[qb] - m_new) : 1.0f;
+        l[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[qb][db] *= alpha;
+        m[qb] = m_new;
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) ref[qb] = m[qb] == -INFINITY ? 0.f : m[qb];
+    // P = exp2(S * cs - ref) -> bf16, row sums of the rounded values
+    bf16x8 pf[QB][KS];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          bf16x8 pk;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][half * 8 + e], cs, -ref[qb]));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][half * 8 + e + 1], cs, -ref[qb]));
+            const bf16x2 pp = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+#if RA_BF16_DOT2SUM
+            rs = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, rs, false);
+#else
+            rs += p0 + p1;
+#endif
+            pk[e] = pp[0];
+            pk[e + 1] = pp[1];
+          }
+          pf[qb][2 * kb + half] = pk;
+        }
+      l[qb] += rs;
+    }
+    // O^T += V^T P^T
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vs_ + off.v_base[db][0] + ks * 16 * ROWB));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vs_ + off.v_base[db][1] + ks * 16 * ROWB));
+        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[qb][ks], o[qb][db], 0, 0, 0);
+      }
+    }
+  };
 
   const int ntk_all = (c + TK - 1) / TK;
   for (int rr = 0; rr < a.r_count; ++rr) {
@@ -172,125 +320,115 @@ __global__ __launch_bounds__(NT, (QB == 1 ? 2 : 1)) void k_attn_bf16(AttnArgs a)
     const int k = ring_block(p, r, a.P);
     const int mode = round_mode(a.layout, a.causal, p, k);
     const int delta = mode == MODE_STRICT ? 1 : 0;
-    // tiles this workgroup must visit: up to the last one with a visible pair for its rows
+    // tiles this workgroup visits: up to the last one with a visible pair for its rows
     int ntk = ntk_all;
     if (mode == MODE_SKIP) ntk = 0;
     else if (mode != MODE_FULL) ntk = (q_wg_last - delta < 0) ? 0 : min(ntk_all, (q_wg_last - delta) / TK + 1);
 
     const int64_t kvo = bh * a.kv_bh_stride + (int64_t)(k - a.kv_base) * a.kv_blk_stride;
-    const __bf16* kp = (const __bf16*)a.k + kvo;
-    const __bf16* vp = (const __bf16*)a.v + kvo;
+    const char* kblk = (const char*)((const __bf16*)a.k + kvo);
+    const char* vblk = (const char*)((const __bf16*)a.v + kvo);
 
     uint64_t st_full = 0, st_diag = 0, st_pairs_uniform = 0;
     uint32_t st_pairs_lane = 0;
 
-    if (ntk > 0) {
-      KVRegs R;
-      load_tile(R, kp, vp, 0, c, tid);
-      store_tile(smem, R, tid);
-      __syncthreads();
-      for (int t = 0; t < ntk; ++t) {
-        const bool more = t + 1 < ntk;
-        if (more) load_tile(R, kp, vp, (t + 1) * TK, c, tid);
-        const char* stage = smem + (t & 1) * STAGE_BYTES;
-        const int x0 = t * TK;
-        const int x_last = min(c, x0 + TK) - 1;
-        // this wavefront's tile class (on its in-range part)
-        const bool skip = !wave_live || (mode != MODE_FULL && x0 > qw_last - delta);
-        const bool full = mode == MODE_FULL || x_last <= qw0 - delta;
-        if (!skip) {
-          const bool need_mask = !full || (x0 + TK > c);
-          if (STATS) {
-            if (full) { ++st_full; st_pairs_uniform += (uint64_t)(qw_last - qw0 + 1) * (x_last - x0 + 1); }
-            else ++st_diag;
-          }
-          // ---- S^T = K Q^T
-          f32x16 s[QB][2];
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) { s[qb][0] = f32x16{}; s[qb][1] = f32x16{}; }
-#pragma unroll
-          for (int dk = 0; dk < 8; ++dk) {
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-              const bf16x8 ka = *reinterpret_cast<const bf16x8*>(stage + k_off(32 * b + l32, 2 * dk + hh));
-#pragma unroll
-              for (int qb = 0; qb < QB; ++qb)
-                s[qb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][dk], s[qb][b], 0, 0, 0);
-            }
-          }
-          // ---- mask (diagonal tiles, ragged edge)
-          if (need_mask) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-              const int y = qw0 + qb * 32 + l32;
-#pragma unroll
-              for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int rg = 0; rg < 16; ++rg) {
-                  const int x = x0 + 32 * b + acc_row(rg, hh);
-                  const bool vis = x < c && (mode == MODE_FULL || x <= y - delta);
-                  if (STATS && !full) st_pairs_lane += (vis && y < c) ? 1u : 0u;
-                  if (!vis) s[qb][b][rg] = -INFINITY;
-                }
-            }
-          }
-          // ---- online softmax; P packed to bf16 in MFMA B-operand order
-          bf16x8 pf[QB][4];
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            float mx = s[qb][0][0];
-#pragma unroll
-            for (int rg = 1; rg < 16; ++rg) mx = fmaxf(mx, s[qb][0][rg]);
-#pragma unroll
-            for (int rg = 0; rg < 16; ++rg) mx = fmaxf(mx, s[qb][1][rg]);
-            mx = pair_max(mx);
-            const float m_new = fmaxf(m[qb], mx * cs);
-            const float ref = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m[qb] - ref);
-            m[qb] = m_new;
-            float rs = 0.f;
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-#pragma unroll
-              for (int half = 0; half < 2; ++half) {
-                bf16x8 pk;
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                  const float p0 = __builtin_amdgcn_exp2f(fmaf(s[qb][b][half * 8 + e], cs, -ref));
-                  const float p1 = __builtin_amdgcn_exp2f(fmaf(s[qb][b][half * 8 + e + 1], cs, -ref));
-                  rs += p0 + p1;
-                  const bf16x2 pp = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
-                  pk[e] = pp[0];
-                  pk[e + 1] = pp[1];
-                }
-                pf[qb][2 * b + half] = pk;
-              }
-            }
-            l[qb] = l[qb] * alpha + rs;
-#pragma unroll
-            for (int db = 0; db < 4; ++db) o[qb][db] *= alpha;
-          }
-          // ---- O^T += V^T P^T
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-              const int dd = 32 * db + l32;
-              const bf16x8 va = *reinterpret_cast<const bf16x8*>(stage + KS_BYTES + vt_off(dd, 2 * ks + hh, 0));
-#pragma unroll
-              for (int qb = 0; qb < QB; ++qb)
-                o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[qb][ks], o[qb][db], 0, 0, 0);
-            }
-          }
-        }
-        if (more) store_tile(smem + ((t + 1) & 1) * STAGE_BYTES, R, tid);
-        __syncthreads();
+    // per-wave tile class: 0 skip; 1 every pair visible; 2 diagonal (element mask, pairs counted
+    // per element); 3 every in-range pair visible but the tile runs past the block end (mask only
+    // the keys past the end)
+    auto tile_class = [&](int t) -> int {
+      const int x0 = t * TK;
+      const int x_last = min(c, x0 + TK) - 1;
+      if (!wave_live || (mode != MODE_FULL && x0 > qw_last - delta)) return 0;
+      const bool full = mode == MODE_FULL || x_last <= qw0 - delta;
+      if (STATS) {
+        if (full) { ++st_full; st_pairs_uniform += (uint64_t)(qw_last - qw0 + 1) * (x_last - x0 + 1); }
+        else ++st_diag;
       }
+      return full ? (x0 + TK <= c ? 1 : 3) : 2;
+    };
+    auto apply_mask = [&](f32x16 (&s)[QB][KB], int t, bool count) __attribute__((always_inline)) {
+      const int x0 = t * TK;
+      const bool full_mode = mode == MODE_FULL;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int y = qw0 + qb * 32 + l32;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int rg = 0; rg < 16; ++rg) {
+            const int x = x0 + 32 * kb + acc_row(rg, hh);
+            const bool vis = x < c && (full_mode || x <= y - delta);
+            if (STATS && count) st_pairs_lane += (vis && y < c) ? 1u : 0u;
+            s[qb][kb][rg] = vis ? s[qb][kb][rg] : -INFINITY;
+          }
+      }
+    };
+
+    if (ntk > 0) {
+#if RA_BF16_PIPE
+      // prologue: K(0), K(1), V(0) into LDS; S(0)
+      dma_tile<A::DMA_PER_WAVE>(kblk, kst(0), 0, c, dko, wave_u);
+      if (ntk > 1) dma_tile<A::DMA_PER_WAVE>(kblk, kst(1), TK, c, dko, wave_u);
+      dma_tile<A::DMA_PER_WAVE>(vblk, vst(0), 0, c, dvo, wave_u);
+      wait_dma_and_barrier();
+      int cls_cur = tile_class(0);
+      if (cls_cur) compute_s(kst(0), sA);
+
+      // one pipelined step: softmax/PV of tile t (in s_cur) and S of tile t+1 (into s_nxt)
+      auto step = [&](int t, f32x16 (&s_cur)[QB][KB], f32x16 (&s_nxt)[QB][KB]) __attribute__((always_inline)) {
+        wait_dma_and_barrier();                       // K(t+1), V(t) landed; stage reuse is safe
+        if (t + 2 < ntk) dma_tile<A::DMA_PER_WAVE>(kblk, kst(t & 1), (t + 2) * TK, c, dko, wave_u);
+        if (t + 1 < ntk) dma_tile<A::DMA_PER_WAVE>(vblk, vst((t + 1) & 1), (t + 1) * TK, c, dvo, wave_u);
+        const int cls_nxt = (t + 1 < ntk) ? tile_class(t + 1) : 0;
+        if (cls_cur >= 2) apply_mask(s_cur, t, cls_cur == 2);
+        if (cls_cur && cls_nxt) {                     // common case: one straight-line block
+          compute_s(kst((t + 1) & 1), s_nxt);
+          softmax_pv(s_cur, vst(t & 1));
+        } else if (cls_cur) {
+          softmax_pv(s_cur, vst(t & 1));
+        } else if (cls_nxt) {
+          compute_s(kst((t + 1) & 1), s_nxt);
+        }
+        cls_cur = cls_nxt;
+      };
+      int t = 0;
+      for (; t + 1 < ntk; t += 2) {
+        step(t, sA, sB);
+        step(t + 1, sB, sA);
+      }
+      if (t < ntk) step(t, sA, sB);
+#else
+      // tile t lives in stage t & 1; its DMA was issued one iteration earlier.  The loop is
+      // unrolled by two so that the stage offsets are compile-time immediates.
+      dma_tile<A::DMA_PER_WAVE>(kblk, kst(0), 0, c, dko, wave_u);
+      dma_tile<A::DMA_PER_WAVE>(vblk, vst(0), 0, c, dvo, wave_u);
+      auto iter = [&](int t, auto stage_c) __attribute__((always_inline)) {
+        constexpr int S = decltype(stage_c)::value;
+        wait_dma_and_barrier();                       // tile t landed; the other stage is free
+        if (t + 1 < ntk) {
+          dma_tile<A::DMA_PER_WAVE>(kblk, smem + (1 - S) * TILE, (t + 1) * TK, c, dko, wave_u);
+          dma_tile<A::DMA_PER_WAVE>(vblk, smem + (3 - S) * TILE, (t + 1) * TK, c, dvo, wave_u);
+        }
+        const int cls = tile_class(t);
+        if (cls) {
+          compute_s(smem + S * TILE, sA);
+          if (cls >= 2) apply_mask(sA, t, cls == 2);
+          softmax_pv(sA, smem + (2 + S) * TILE);
+        }
+      };
+      int t = 0;
+      for (; t + 1 < ntk; t += 2) {
+        iter(t, std::integral_constant<int, 0>{});
+        iter(t + 1, std::integral_constant<int, 1>{});
+      }
+      if (t < ntk) iter(t, std::integral_constant<int, 0>{});
+#endif
+      __syncthreads();                                // LDS stages free for the next round
     }
 
     if (STATS && wave_live) {
       unsigned long long pairs = st_pairs_lane;
-      for (int off = 32; off > 0; off >>= 1) pairs += __shfl_xor(pairs, off);
+      for (int off2 = 32; off2 > 0; off2 >>= 1) pairs += __shfl_xor(pairs, off2);
       if (lane == 0) {
         ra_round_stats_t* st = a.stats_single ? a.stats : a.stats + ((int64_t)p * a.P + r);
         atomicAdd((unsigned long long*)&st->unmasked_pairs, (unsigned long long)(pairs + st_pairs_uniform));
@@ -339,23 +477,24 @@ __global__ __launch_bounds__(NT, (QB == 1 ? 2 : 1)) void k_attn_bf16(AttnArgs a)
   }
 }
 
-constexpr int QB_DEFAULT = 1;
+constexpr int QB_SEL = RA_BF16_QB;
+constexpr int TK_SEL = RA_BF16_TK;
 
 }  // namespace
 
 bool attn_bf16_supported(int64_t d) { return d == D; }
-void attn_bf16_tile(int* tq, int* tk) { *tq = 32 * QB_DEFAULT; *tk = TK; }
+void attn_bf16_tile(int* tq, int* tk) { *tq = 32 * QB_SEL; *tk = TK_SEL; }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int d, hipStream_t s) {
   if (d != D) return hipErrorInvalidValue;
-  constexpr int TQ = NW * 32 * QB_DEFAULT;
+  constexpr int TQ = NW * 32 * QB_SEL;
   const int64_t blocks = (int64_t)((a.c + TQ - 1) / TQ) * a.BH * a.n_dev;
   if (blocks * NT >= (1ll << 32)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks);
   if (a.stats)
-    hipLaunchKernelGGL((k_attn_bf16<QB_DEFAULT, true>), grid, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((k_attn_bf16<QB_SEL, TK_SEL, true>), grid, dim3(NT), 0, s, a);
   else
-    hipLaunchKernelGGL((k_attn_bf16<QB_DEFAULT, false>), grid, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((k_attn_bf16<QB_SEL, TK_SEL, false>), grid, dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
