@@ -277,13 +277,12 @@ def tile_counts_closed_form(layout: str, j: int, k: int, c: int, tq: int, tk: in
     if layout == CONTIGUOUS and j < k:
         return 0, 0, total
     delta = 1 if (layout == STRIPED and j < k) else 0
-    full = diag = 0
-    for ty in range(nt_q):
-        y0, y1 = ty * tq, min(c, ty * tq + tq)
-        for tx in range(nt_k):
-            x0, x1 = tx * tk, min(c, tx * tk + tk)
-            if x1 - 1 <= y0 - delta:
-                full += 1
-            elif x0 <= y1 - 1 - delta:
-                diag += 1
+    y0 = np.arange(nt_q, dtype=np.int64)[:, None] * tq          # tile rows  [y0, y1)
+    y1 = np.minimum(c, y0 + tq)
+    x0 = np.arange(nt_k, dtype=np.int64)[None, :] * tk          # tile cols  [x0, x1)
+    x1 = np.minimum(c, x0 + tk)
+    is_full = (x1 - 1) <= (y0 - delta)
+    is_diag = ~is_full & (x0 <= (y1 - 1 - delta))
+    full = int(is_full.sum())
+    diag = int(is_diag.sum())
     return full, diag, total - full - diag

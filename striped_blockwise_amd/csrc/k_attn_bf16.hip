@@ -41,7 +41,13 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int D = 128;          // head dim
 constexpr int ROWB = D * 2;     // bytes per K / V row
-constexpr int NW = 4;           // wavefronts per workgroup
+#ifndef RA_BF16_NW
+#define RA_BF16_NW 4            // wavefronts per workgroup
+#endif
+#ifndef RA_BF16_XMAP
+#define RA_BF16_XMAP 1          // 1: XCD-major block order (one (head, device) stream per XCD)
+#endif
+constexpr int NW = RA_BF16_NW;  // wavefronts per workgroup
 constexpr int NT = NW * 64;     // threads per workgroup
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -174,11 +180,24 @@ __global__ __launch_bounds__(NT, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) {
   const int hh = lane >> 5;
   const int c = a.c;
 
+  // Block -> (stream = (device, head), q-tile).  Blocks are dispatched round-robin over the 8
+  // XCDs (block i on XCD i % 8), each with its own L2.  XCD-major order gives XCD x the streams
+  // x, x+8, x+16, ... one after another, all q-tiles of a stream together, so the workgroups
+  // resident on an XCD read the same K/V blocks at about the same time.  Within a stream the
+  // q-tiles with the most causal work go first.
   const int nqt = (c + TQ - 1) / TQ;
-  const int bh = blockIdx.x % a.BH;      // heads fastest: block i runs on XCD i % 8, so the
-  const int rest = blockIdx.x / a.BH;    // q-tiles of one head share that XCD's L2
-  const int dev = rest % a.n_dev;
-  const int qt = nqt - 1 - rest / a.n_dev;   // most causal work first
+  int stream, qt;
+  if (RA_BF16_XMAP && a.xcd_major) {
+    const int x = blockIdx.x & 7;
+    const int sq = blockIdx.x >> 3;
+    stream = (sq / nqt) * 8 + x;
+    qt = nqt - 1 - sq % nqt;
+  } else {
+    stream = blockIdx.x % (a.BH * a.n_dev);
+    qt = nqt - 1 - blockIdx.x / (a.BH * a.n_dev);
+  }
+  const int bh = stream % a.BH;
+  const int dev = stream / a.BH;
   const int p = a.p_begin + dev;
   const int q_wg0 = qt * TQ;
   const int q_wg_last = min(c, q_wg0 + TQ) - 1;
@@ -491,10 +510,12 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int d, hipStream_t s) {
   const int64_t blocks = (int64_t)((a.c + TQ - 1) / TQ) * a.BH * a.n_dev;
   if (blocks * NT >= (1ll << 32)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks);
+  AttnArgs b = a;
+  b.xcd_major = ((int64_t)a.BH * a.n_dev) % 8 == 0 ? 1 : 0;
   if (a.stats)
-    hipLaunchKernelGGL((k_attn_bf16<QB_SEL, TK_SEL, true>), grid, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((k_attn_bf16<QB_SEL, TK_SEL, true>), grid, dim3(NT), 0, s, b);
   else
-    hipLaunchKernelGGL((k_attn_bf16<QB_SEL, TK_SEL, false>), grid, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((k_attn_bf16<QB_SEL, TK_SEL, false>), grid, dim3(NT), 0, s, b);
   return hipGetLastError();
 }
 

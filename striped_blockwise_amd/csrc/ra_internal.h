@@ -57,6 +57,7 @@ struct AttnArgs {
   int o_f32;              // 1: o is float32, 0: bf16
   ra_round_stats_t* stats;  // nullable
   int stats_single;       // 1: one entry (ra_round), 0: [P][P] indexed [p][r]
+  int xcd_major;          // set by the bf16 launcher: block order (see k_attn_bf16.hip)
 };
 
 hipError_t launch_permute(const void* src, void* dst, int64_t BH, int64_t n, int64_t row_bytes,

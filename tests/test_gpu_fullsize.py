@@ -1,0 +1,166 @@
+"""GPU parity at full workload sizes, in the launch configuration bench.py times.
+
+* 256K-token share (n = 262144, P = 8, H = 32, d = 128, bf16): device 7's query block against all
+  8 K/V blocks with ra_forward, contiguous and striped (the striped inputs go through
+  ra_permute first, as in the timed step).  Every device of both layouts is also run once, so
+  the whole sequence's striped output, un-permuted on the GPU, can be compared with the
+  contiguous one.
+* 1M-token stress (n = 1048576, P = 32, H = 8, 1% of K rows x8): device 31, striped, all 32
+  rounds streamed through ra_round + ra_merge, and the same share fused with ra_forward.
+
+Floating-point outputs are checked against the fp64 oracle on sampled query rows (the oracle
+computes each sampled row against all keys in token order; attention does not depend on the
+order of the keys, only on their positions).  Integer outputs (permutation, work counters) are
+checked exactly.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import attention as OA
+from oracle import ring as OR
+from tests._gpu_util import compare, need_gpu, np64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ra():
+    need_gpu()
+    import striped_blockwise_amd as m
+    return m
+
+
+def _sel(t: torch.Tensor, heads, rows) -> torch.Tensor:
+    """t[0, heads][:, rows] for a GPU tensor with numpy/list indices."""
+    return t[0].index_select(0, torch.tensor(heads, device=t.device)).index_select(
+        1, torch.as_tensor(np.asarray(rows), device=t.device))
+
+
+def _sample_rows(c: int, k: int = 58, seed: int = 1234) -> np.ndarray:
+    fixed = np.array([0, 1, 2, c // 2, c - 2, c - 1])
+    rnd = np.random.default_rng(seed).choice(c, size=k, replace=False)
+    return np.unique(np.concatenate([fixed, rnd]))
+
+
+def _oracle_rows(w, heads, tokens):
+    """fp64 attention for the given query tokens (global positions), per head, all keys."""
+    o_ref, l_ref = [], []
+    for h in heads:
+        q, k, v = workloads.qkv(w, heads=[h])
+        o, l = OA.attention(q[:, :, torch.from_numpy(tokens)], k, v, True, pos_q=tokens, pos_k=np.arange(w.n))
+        o_ref.append(o[0, 0])
+        l_ref.append(l[0, 0])
+    return np.stack(o_ref), np.stack(l_ref)
+
+
+def _expected_stats_row(layout, P, c, p, BH, tq, tk):
+    out = np.zeros((P, 4), dtype=np.int64)
+    for r in range(P):
+        kk = OR.kv_block(p, r, P)
+        pairs = OR.work_closed_form(layout, p, kk, c, True)
+        full, diag, skip = OR.tile_counts_closed_form(layout, p, kk, c, tq, tk, True)
+        out[r] = [pairs * BH, full * BH, diag * BH, skip * BH]
+    return out
+
+
+@pytest.fixture(scope="module")
+def share(ra):
+    w = workloads.get("share_n256k")
+    print(f"[fullsize] generating {w.name}", flush=True)
+    q, k, v = (t.cuda() for t in workloads.qkv(w))
+    torch.cuda.synchronize()
+    yield w, q, k, v
+    del q, k, v
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+def test_share256k_device7(ra, share, layout):
+    w, q, k, v = share
+    P, c, p = w.P, w.c, w.device
+    order = OR.layout_order(w.n, P, layout)
+    if layout == "striped":
+        qs, ks, vs = (ra.permute(t, P) for t in (q, k, v))
+        ids = ra.permute_ids(workloads.positions(w.n).cuda(), P)
+        torch.cuda.synchronize()
+        idx = torch.from_numpy(order).cuda()
+        assert torch.equal(ids.cpu(), torch.from_numpy(order)), "position-ID permutation"
+        assert torch.equal(qs[:, 5], q[:, 5].index_select(1, idx)), "Q permutation (head 5)"
+        assert torch.equal(vs[:, 31], v[:, 31].index_select(1, idx)), "V permutation (head 31)"
+    else:
+        qs, ks, vs = q, k, v
+    stats = ra.new_stats(P)
+    o, lse = ra.forward(qs, ks, vs, P, layout, True, p_begin=p, p_end=p + 1, stats=stats)
+    torch.cuda.synchronize()
+    tq, tk = ra.tile_shape(ra.BF16, w.d)
+    got = stats.cpu().numpy()
+    assert np.array_equal(got[p], _expected_stats_row(layout, P, c, p, w.B * w.H, tq, tk)), got[p]
+    assert not got[:p].any() and not got[p + 1:].any()
+    rows = _sample_rows(c)
+    heads = [0, 9, 22, 31]
+    tokens = order[p * c + rows]
+    o_ref, l_ref = _oracle_rows(w, heads, tokens)
+    compare(_sel(o, heads, rows).float(), _sel(lse, heads, rows), o_ref, l_ref, "bf16",
+            f"share256k {layout} device {p}")
+    del qs, ks, vs
+
+
+def test_share256k_whole_sequence_equivariance(ra, share):
+    """Striped over all devices, un-permuted, equals contiguous over all devices."""
+    w, q, k, v = share
+    P = w.P
+    o_c, l_c = ra.forward(q, k, v, P, "contiguous", True, o_dtype=torch.float32)
+    qs, ks, vs = (ra.permute(t, P) for t in (q, k, v))
+    o_s, l_s = ra.forward(qs, ks, vs, P, "striped", True, o_dtype=torch.float32)
+    del qs, ks, vs
+    o_u = ra.permute(o_s, P, inverse=True)
+    l_u = ra.permute(l_s, P, dim=-1, inverse=True)
+    del o_s, l_s
+    torch.cuda.synchronize()
+    err_o = float((o_u - o_c).abs().max())
+    err_l = float((l_u - l_c).abs().max())
+    assert err_o <= 2e-2 and err_l <= 1e-3, (err_o, err_l)
+    # and both against the oracle on a few tokens spread over the sequence
+    tokens = np.array([0, 1, 7, 8, 4095, 32767, 32768, 131071, 200003, w.n - 2, w.n - 1])
+    heads = [3, 17]
+    o_ref, l_ref = _oracle_rows(w, heads, tokens)
+    compare(_sel(o_u, heads, tokens), _sel(l_u, heads, tokens), o_ref, l_ref, "bf16", "whole-sequence striped")
+    compare(_sel(o_c, heads, tokens), _sel(l_c, heads, tokens), o_ref, l_ref, "bf16", "whole-sequence contiguous")
+
+
+def test_stress1m_streamed_rounds_and_merge(ra):
+    w = workloads.get("stress_n1m")
+    P, c, p = w.P, w.c, w.device
+    print(f"[fullsize] generating {w.name}", flush=True)
+    q, k, v = (t.cuda() for t in workloads.qkv(w))
+    qs, ks, vs = (ra.permute(t, P) for t in (q, k, v))
+    del q, k, v
+    acc_o = torch.zeros((w.B, w.H, c, w.d), dtype=torch.float32, device="cuda")
+    acc_l = torch.full((w.B, w.H, c), float("-inf"), device="cuda")
+    tq, tk = ra.tile_shape(ra.BF16, w.d)
+    exp_stats = _expected_stats_row("striped", P, c, p, w.B * w.H, tq, tk)
+    for r in range(P):
+        kk = OR.kv_block(p, r, P)
+        st = torch.zeros(4, dtype=torch.int64, device="cuda")
+        po, pl = ra.round(qs[:, :, p * c:(p + 1) * c], ks[:, :, kk * c:(kk + 1) * c], vs[:, :, kk * c:(kk + 1) * c],
+                          P, p, kk, "striped", True, stats=st)
+        ra.merge(acc_o, acc_l, po, pl)
+        assert st.cpu().numpy().tolist() == exp_stats[r].tolist(), r
+    o_f, l_f = ra.forward(qs, ks, vs, P, "striped", True, p_begin=p, p_end=p + 1, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    del qs, ks, vs
+    order = OR.layout_order(w.n, P, "striped")
+    rows = _sample_rows(c, k=26)
+    heads = [0, 3, 7]
+    tokens = order[p * c + rows]
+    o_ref, l_ref = _oracle_rows(w, heads, tokens)
+    compare(_sel(acc_o, heads, rows), _sel(acc_l, heads, rows), o_ref, l_ref, "bf16", "stress1m streamed")
+    compare(_sel(o_f, heads, rows), _sel(l_f, heads, rows), o_ref, l_ref, "bf16", "stress1m fused")
+    assert float((acc_o - o_f).abs().max()) <= 2e-2
+    assert float((acc_l - l_f).abs().max()) <= 1e-3
+    del acc_o, acc_l, o_f, l_f
+    torch.cuda.empty_cache()
