@@ -305,6 +305,27 @@ def main(argv=None) -> int:
             f"({merge_bytes / (mavg * 1e-3) / 1e9:.0f} GB/s); permute {perm_ms:.3f} ms "
             f"({perm_bytes / (perm_ms * 1e-3) / 1e9:.0f} GB/s)")
 
+    if not args.no_extras:
+        # context: a plain library GEMM (torch.matmul -> hipBLASLt), bf16, square 8192, on the
+        # same box in the same run -- what dense bf16 matrix-core work sustains here
+        g = 8192
+        ga = torch.randn((g, g), device=dev, dtype=torch.bfloat16)
+        gb = torch.randn((g, g), device=dev, dtype=torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(ga, gb)
+        torch.cuda.synchronize()
+        reps = 40
+        a.record()
+        for _ in range(reps):
+            torch.matmul(ga, gb)
+        b.record()
+        torch.cuda.synchronize()
+        gemm_ms = a.elapsed_time(b) / reps
+        result["context_gemm"] = {"op": "torch.matmul bf16 8192x8192x8192 (hipBLASLt)", "ms": round(gemm_ms, 4),
+                                  "tflops": round(2.0 * g ** 3 / (gemm_ms * 1e-3) / 1e12, 1)}
+        log(f"[bench] bf16 GEMM 8192^3: {result['context_gemm']['tflops']} TFLOP/s")
+        del ga, gb
+
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(w, "striped")

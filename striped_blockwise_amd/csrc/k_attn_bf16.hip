@@ -9,8 +9,8 @@
 //
 // Data flow per TK-key tile:
 //   HBM -> LDS by DMA (buffer_load ... lds, 16 B per lane), K and V both row-major with a
-//   16-byte-chunk XOR swizzle; no registers or VALU work on the way in.  K and V each have two
-//   LDS stages; the loads for tile t+2 (K) and t+1 (V) are in flight while tile t computes.
+//   per-row XOR swizzle of their 16-byte chunks; no registers or VALU work on the way in.  Two
+//   LDS stages: the next tile's load is in flight while this tile computes.
 //   S^T = K Q^T on MFMA: A = 32 K rows from LDS, B = the wavefront's Q columns in registers.
 //   In this orientation each lane owns one query, so the row max / row sum are in-lane
 //   reductions plus one v_permlane32_swap with the other half of the wavefront.
@@ -18,8 +18,6 @@
 //   O^T += V^T P^T on MFMA: A = V^T, read from the row-major V tile with ds_read_b64_tr_b16
 //   (which transposes 4x4 blocks of 16-bit elements across lanes), B = P straight from the
 //   score registers (the contraction index is permuted identically on both operands).
-//   Software pipelining: the S MFMAs of tile t+1 are issued in the same basic block as the
-//   softmax VALU work of tile t, so the matrix cores and the vector ALUs overlap.
 // The running max is only raised when a tile's max exceeds it by more than 2^8 (in exp2
 // units), so the rescale of O (64-128 multiplies per lane) is rare; the result is exact either
 // way because O, l and the reference max always stay consistent.
@@ -58,12 +56,6 @@ constexpr float TAU = 8.0f;     // lazy-rescale threshold, log2 units
 #endif
 #ifndef RA_BF16_TK
 #define RA_BF16_TK 32           // keys per tile
-#endif
-#ifndef RA_BF16_PIPE
-#define RA_BF16_PIPE 0          // 1: S of tile t+1 overlaps the softmax of tile t
-#endif
-#ifndef RA_BF16_DOT2SUM
-#define RA_BF16_DOT2SUM 0       // 1: row sums with v_dot2 on the rounded probabilities
 #endif
 #ifndef RA_BF16_OCC
 #define RA_BF16_OCC 2           // target wavefronts per SIMD
@@ -232,13 +224,9 @@ __global__ __launch_bounds__(NT, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) { m[qb] = -INFINITY; l[qb] = 0.f; }
   const float cs = a.scale * LOG2E;
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // S^T tile of one wavefront: [qb][32-key block]
   f32x16 sA[QB][KB];
-#if RA_BF16_PIPE
-  f32x16 sB[QB][KB];
-#endif
 
   // S^T = K Q^T for one tile.  All K fragments of a 32-key block are requested from LDS before
   // the first MFMA that needs one (the scheduling barrier keeps the compiler from interleaving
@@ -306,11 +294,7 @@ __global__ __launch_bounds__(NT, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) {
             const float p0 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][half * 8 + e], cs, -ref[qb]));
             const float p1 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][half * 8 + e + 1], cs, -ref[qb]));
             const bf16x2 pp = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
-#if RA_BF16_DOT2SUM
-            rs = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, rs, false);
-#else
             rs += p0 + p1;
-#endif
             pk[e] = pp[0];
             pk[e + 1] = pp[1];
           }
@@ -384,39 +368,6 @@ __global__ __launch_bounds__(NT, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) {
     };
 
     if (ntk > 0) {
-#if RA_BF16_PIPE
-      // prologue: K(0), K(1), V(0) into LDS; S(0)
-      dma_tile<A::DMA_PER_WAVE>(kblk, kst(0), 0, c, dko, wave_u);
-      if (ntk > 1) dma_tile<A::DMA_PER_WAVE>(kblk, kst(1), TK, c, dko, wave_u);
-      dma_tile<A::DMA_PER_WAVE>(vblk, vst(0), 0, c, dvo, wave_u);
-      wait_dma_and_barrier();
-      int cls_cur = tile_class(0);
-      if (cls_cur) compute_s(kst(0), sA);
-
-      // one pipelined step: softmax/PV of tile t (in s_cur) and S of tile t+1 (into s_nxt)
-      auto step = [&](int t, f32x16 (&s_cur)[QB][KB], f32x16 (&s_nxt)[QB][KB]) __attribute__((always_inline)) {
-        wait_dma_and_barrier();                       // K(t+1), V(t) landed; stage reuse is safe
-        if (t + 2 < ntk) dma_tile<A::DMA_PER_WAVE>(kblk, kst(t & 1), (t + 2) * TK, c, dko, wave_u);
-        if (t + 1 < ntk) dma_tile<A::DMA_PER_WAVE>(vblk, vst((t + 1) & 1), (t + 1) * TK, c, dvo, wave_u);
-        const int cls_nxt = (t + 1 < ntk) ? tile_class(t + 1) : 0;
-        if (cls_cur >= 2) apply_mask(s_cur, t, cls_cur == 2);
-        if (cls_cur && cls_nxt) {                     // common case: one straight-line block
-          compute_s(kst((t + 1) & 1), s_nxt);
-          softmax_pv(s_cur, vst(t & 1));
-        } else if (cls_cur) {
-          softmax_pv(s_cur, vst(t & 1));
-        } else if (cls_nxt) {
-          compute_s(kst((t + 1) & 1), s_nxt);
-        }
-        cls_cur = cls_nxt;
-      };
-      int t = 0;
-      for (; t + 1 < ntk; t += 2) {
-        step(t, sA, sB);
-        step(t + 1, sB, sA);
-      }
-      if (t < ntk) step(t, sA, sB);
-#else
       // tile t lives in stage t & 1; its DMA was issued one iteration earlier.  The loop is
       // unrolled by two so that the stage offsets are compile-time immediates.
       dma_tile<A::DMA_PER_WAVE>(kblk, kst(0), 0, c, dko, wave_u);
@@ -441,7 +392,6 @@ __global__ __launch_bounds__(NT, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) {
         iter(t + 1, std::integral_constant<int, 1>{});
       }
       if (t < ntk) iter(t, std::integral_constant<int, 0>{});
-#endif
       __syncthreads();                                // LDS stages free for the next round
     }
 
