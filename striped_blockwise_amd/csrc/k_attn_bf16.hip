@@ -95,7 +95,8 @@ struct Attn {
   static constexpr int KB = TK / 32;              // 32-key MFMA blocks per tile
   static constexpr int KS = TK / 16;              // 16-key MFMA k-steps per tile (P V)
   static constexpr int TILE = TK * ROWB;          // bytes of one K or V tile
-  static constexpr int DMA_PER_WAVE = TILE / (NW * 1024);   // 1 KB per wave-wide DMA
+  static constexpr int DMA_SEGS = TILE / 1024;                        // 1 KB wave-wide DMAs per tile
+  static constexpr int DMA_PER_WAVE = (DMA_SEGS + NW - 1) / NW;       // segments wave w: w, w+NW, ...
 
   // Per-lane constant parts of the LDS addresses.
   int k_base[8];       // K operand: row l32, chunk (2 dk + hh)
@@ -127,15 +128,16 @@ struct Attn {
 // offsets are loop constants and rows past the end of the block are out of range: the buffer
 // unit returns zeros for them, which land in LDS (zero keys are masked out of the scores, and
 // zero values contribute nothing).
-template <int DMA_PER_WAVE>
+template <int DMA_PER_WAVE, int DMA_SEGS>
 __device__ __forceinline__ void dma_tile(const char* block, char* stage, int x0, int c,
                                          const unsigned* voff, int wave_u) {
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(block + (int64_t)x0 * ROWB), 0, (c - x0) * ROWB, 0x00020000);
 #pragma unroll
   for (int i = 0; i < DMA_PER_WAVE; ++i) {
-    const int seg = wave_u * DMA_PER_WAVE + i;            // 1 KB segment = 4 rows
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(stage + seg * 1024), 16, voff[i], 0, 0, 0);
+    const int seg = wave_u + i * NW;                      // 1 KB segment = 4 rows
+    if (DMA_SEGS % NW == 0 || seg < DMA_SEGS)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(stage + seg * 1024), 16, voff[i], 0, 0, 0);
   }
 }
 
@@ -146,7 +148,7 @@ template <int DMA_PER_WAVE, bool IS_V>
 __device__ __forceinline__ void dma_offsets(unsigned* voff, int wave_u, int lane) {
 #pragma unroll
   for (int i = 0; i < DMA_PER_WAVE; ++i) {
-    const int row = (wave_u * DMA_PER_WAVE + i) * 4 + (lane >> 4);
+    const int row = (wave_u + i * NW) * 4 + (lane >> 4);
     const int mask = IS_V ? v_swz(row) : k_swz(row);
     voff[i] = (unsigned)(row * ROWB + (((lane & 15) ^ mask) << 4));
   }
@@ -370,14 +372,14 @@ __global__ __launch_bounds__(NT, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) {
     if (ntk > 0) {
       // tile t lives in stage t & 1; its DMA was issued one iteration earlier.  The loop is
       // unrolled by two so that the stage offsets are compile-time immediates.
-      dma_tile<A::DMA_PER_WAVE>(kblk, kst(0), 0, c, dko, wave_u);
-      dma_tile<A::DMA_PER_WAVE>(vblk, vst(0), 0, c, dvo, wave_u);
+      dma_tile<A::DMA_PER_WAVE, A::DMA_SEGS>(kblk, kst(0), 0, c, dko, wave_u);
+      dma_tile<A::DMA_PER_WAVE, A::DMA_SEGS>(vblk, vst(0), 0, c, dvo, wave_u);
       auto iter = [&](int t, auto stage_c) __attribute__((always_inline)) {
         constexpr int S = decltype(stage_c)::value;
         wait_dma_and_barrier();                       // tile t landed; the other stage is free
         if (t + 1 < ntk) {
-          dma_tile<A::DMA_PER_WAVE>(kblk, smem + (1 - S) * TILE, (t + 1) * TK, c, dko, wave_u);
-          dma_tile<A::DMA_PER_WAVE>(vblk, smem + (3 - S) * TILE, (t + 1) * TK, c, dvo, wave_u);
+          dma_tile<A::DMA_PER_WAVE, A::DMA_SEGS>(kblk, smem + (1 - S) * TILE, (t + 1) * TK, c, dko, wave_u);
+          dma_tile<A::DMA_PER_WAVE, A::DMA_SEGS>(vblk, smem + (3 - S) * TILE, (t + 1) * TK, c, dvo, wave_u);
         }
         const int cls = tile_class(t);
         if (cls) {
