@@ -19,6 +19,7 @@ Also measured in the same run (reported as extra fields, never as ``value``):
   * cpu_baseline: the fp64 CPU oracle on a bounded sample of the same share.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+       python bench.py --sweep      (striped/ring speedup vs sequence length; its own JSON line)
 """
 from __future__ import annotations
 
@@ -115,6 +116,50 @@ def cpu_baseline(w, layout: str, budget_s: float = 12.0):
     }
 
 
+def sweep(torch, ra, dev, P: int = 8, H: int = 8, d: int = 128,
+          lengths=(16384, 32768, 65536, 131072, 262144, 524288, 1048576)) -> int:
+    """Fused-forward time of the last device (most causal work under the contiguous layout)
+    for both layouts as the sequence grows: the attention-only version of the Striped
+    Attention review's speedup-vs-length table (which measures whole training steps)."""
+    rows = []
+    for n in lengths:
+        c = n // P
+        p = P - 1
+        gen = torch.Generator(device=dev).manual_seed(n)
+        q, k, v = (torch.randn((1, H, n, d), generator=gen, device=dev).mul_(0.5).to(torch.bfloat16)
+                   for _ in range(3))
+        qs, ks, vs = (ra.permute(t, P) for t in (q, k, v))
+        o = torch.empty((1, H, c, d), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((1, H, c), dtype=torch.float32, device=dev)
+        res = {"n": n, "c": c}
+        for layout, args_ in (("contiguous", (q, k, v)), ("striped", (qs, ks, vs))):
+            pairs = sum(useful_pairs(layout, P, c, p))
+            ra.forward(*args_, P, layout, True, p_begin=p, p_end=p + 1, out=(o, lse))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = max(2, min(20, int(2e13 / (4.0 * d * H * pairs))))
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                ra.forward(*args_, P, layout, True, p_begin=p, p_end=p + 1, out=(o, lse))
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            res[layout + "_ms"] = round(ms, 4)
+            res[layout + "_tflops"] = round(4.0 * d * H * pairs / (ms * 1e-3) / 1e12, 1)
+        res["speedup"] = round(res["contiguous_ms"] / res["striped_ms"], 4)
+        res["ideal_speedup"] = round(sum(useful_pairs("contiguous", P, c, p)) / sum(useful_pairs("striped", P, c, p)), 5)
+        log(f"[sweep] n={n}: contiguous {res['contiguous_ms']:.3f} ms, striped {res['striped_ms']:.3f} ms, "
+            f"speedup {res['speedup']:.3f} (ideal {res['ideal_speedup']})")
+        rows.append(res)
+        del q, k, v, qs, ks, vs, o, lse
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "striped/ring attention-only speedup vs sequence length, 1 GPU",
+                      "config": {"P": P, "device": P - 1, "B": 1, "H": H, "d": d, "dtype": "bf16",
+                                 "data": "synthetic N(0,1)*0.5 (GPU generator)"},
+                      "sweep": rows}), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,6 +168,8 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="share_n256k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="only the timed striped steps")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the default line: striped/ring speedup and TFLOP/s vs sequence length")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -141,6 +188,8 @@ def main(argv=None) -> int:
     ra.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.sweep:
+        return sweep(torch, ra, dev)
     w = workloads.get(args.workload)
     P, c, d, H, B = w.P, w.c, w.d, w.H, w.B
     p = w.device if w.device is not None else P - 1
