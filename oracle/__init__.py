@@ -21,9 +21,12 @@ Modules:
   attention  -- the plain definition: softmax(Q K^T / sqrt(d) + C) V and its log-sum-exp.
   ring       -- layouts, the ring schedule, GetMask, the blockwise online-softmax emulation,
                 the log-sum-exp merge, and the integer work / tile counts.
+  backward   -- gradients dQ, dK, dV: autograd of the definition, and the per-(query block,
+                K/V block) chain rule a ring runs, driven by the forward's log-sum-exp.
 
 Pins: every function here is checked by ``tests/test_oracle_pins.py`` against closed forms,
 a library routine (torch's scaled_dot_product_attention in fp64), brute force on tiny inputs,
-and the worked partition example printed in the Striped Attention review.
+and the worked partition example printed in the Striped Attention review.  The gradients are
+pinned by ``tests/test_oracle_backward_pins.py`` (finite differences, closed forms, invariants).
 """
-from . import attention, ring  # noqa: F401
+from . import attention, backward, ring  # noqa: F401
