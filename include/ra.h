@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define RA_ABI_VERSION 1
+#define RA_ABI_VERSION 2
 
 typedef int32_t ra_status_t;
 enum {
@@ -151,6 +151,53 @@ ra_status_t ra_merge(float* o_acc, float* lse_acc, const float* o_part, const fl
 ra_status_t ra_forward(const ra_problem_t* prob, const void* q, const void* k, const void* v,
                        int32_t p_begin, int32_t p_end, void* o, int32_t o_dtype, float* lse,
                        ra_round_stats_t* stats, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Backward pass.  The pages describe the forward only; the gradients are those of its
+ * definition O = softmax(Q K^T * scale + C) V (Striped Attention review, "核心公式"; Ring
+ * Attention review, step 3).  With the forward's LSE L of each query row and
+ * D = rowsum(O * dO), every (query block p, K/V block k) pair contributes independently:
+ *   P = exp(S + C - L), dP = dO V^T, dS = P * (dP - D),
+ *   dQ_p += scale * dS K_k,  dK_k += scale * dS^T Q_p,  dV_k += P^T dO_p,
+ * with the pair's GetMask deciding C (Striped Attention review, "GetMask 函数").  In a ring,
+ * dQ stays on device p while dK, dV travel with their K/V block (Ring Attention review, step
+ * 2), collecting one contribution per device.  Gradients are float32; Q, K, V and dO share the
+ * problem's dtype.  No atomics: results are deterministic run to run.
+ * ------------------------------------------------------------------------------------------- */
+
+/* Backward row term D_i = sum_e O[i, e] * dO[i, e] for `rows` rows of d values.
+ *   o: [rows, d] in o_dtype (RA_BF16 or RA_F32), the forward output; dout: [rows, d] in
+ *   dout_dtype; delta: [rows] float32 (written).  Arrays contiguous; o and dout 16-byte (f32)
+ *   or 8-byte (bf16) aligned when d % 4 == 0, else element aligned. */
+ra_status_t ra_bwd_delta(const void* o, int32_t o_dtype, const void* dout, int32_t dout_dtype,
+                         int64_t rows, int64_t d, float* delta, void* stream);
+
+/* Backward of one ring round: the query block of device p against the K/V block kv.
+ *   q, dout: device p's rows, B*H matrices of c x d, q_stride_bh elements apart
+ *   k, v:    block kv, B*H matrices of c x d, kv_stride_bh elements apart
+ *   lse, delta: device p's rows, B*H vectors of c float32, row_stride_bh elements apart;
+ *            lse is the FINAL log-sum-exp of the rows over all keys (ra_forward's, or the
+ *            ra_merge result), not a round partial; delta from ra_bwd_delta
+ *   dq_acc:  [B, H, c, d] float32, contiguous: this pair's dQ contribution is ADDED
+ *   dk_acc, dv_acc: [B, H, c, d] float32, contiguous: dK, dV contributions ADDED
+ * A pair with no visible key (contiguous block from a later device) adds nothing. */
+ra_status_t ra_backward_round(const ra_problem_t* prob, const void* q, const void* k,
+                              const void* v, const void* dout, const float* lse,
+                              const float* delta, int64_t q_stride_bh, int64_t kv_stride_bh,
+                              int64_t row_stride_bh, int32_t p, int32_t kv, float* dq_acc,
+                              float* dk_acc, float* dv_acc, void* stream);
+
+/* All rounds of the devices p_begin <= p < p_end, fused (the backward of ra_forward).
+ *   q, k, v: full [B, H, n, d] tensors in layout order (contiguous)
+ *   dout:    [B, H, m, d], m = (p_end - p_begin) * c, rows of device p_begin first
+ *   lse, delta: [B, H, m] float32 (ra_forward's lse; ra_bwd_delta)
+ *   dq:      [B, H, m, d] float32, written
+ *   dk, dv:  [B, H, n, d] float32, written: the gradient that the queries of devices
+ *            p_begin..p_end-1 send to every key (the full gradient when the range is 0..P)
+ * Every output element is written exactly once, by one workgroup, in a fixed order. */
+ra_status_t ra_backward(const ra_problem_t* prob, const void* q, const void* k, const void* v,
+                        const void* dout, const float* lse, const float* delta, int32_t p_begin,
+                        int32_t p_end, float* dq, float* dk, float* dv, void* stream);
 
 #ifdef __cplusplus
 }

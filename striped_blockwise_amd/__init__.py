@@ -16,7 +16,8 @@ import torch
 
 __all__ = [
     "CONTIGUOUS", "STRIPED", "BF16", "F32", "lib", "abi_version", "check", "tile_shape",
-    "permute", "permute_ids", "round", "merge", "forward", "new_stats", "RaError",
+    "permute", "permute_ids", "round", "merge", "forward", "new_stats", "bwd_delta",
+    "backward_round", "backward", "RaError",
 ]
 
 CONTIGUOUS, STRIPED = 0, 1
@@ -51,6 +52,10 @@ _SIGS = {
     "ra_round": (_i32, [_P, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
     "ra_merge": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _vp]),
     "ra_forward": (_i32, [_P, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _vp, _vp]),
+    "ra_bwd_delta": (_i32, [_vp, _i32, _vp, _i32, _i64, _i64, _vp, _vp]),
+    "ra_backward_round": (_i32, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32,
+                                 _vp, _vp, _vp, _vp]),
+    "ra_backward": (_i32, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp]),
 }
 
 
@@ -270,3 +275,116 @@ def forward(q, k, v, P: int, layout="contiguous", causal=True, p_begin: int = 0,
                                 _ptr(o), _dtype_code(o_dtype), _ptr(lse), _ptr(stats), _vp(_stream(dev))),
                "ra_forward")
     return o, lse
+
+
+def _row_stride(t: torch.Tensor, name: str):
+    if t.dim() != 3 or t.dtype != torch.float32:
+        raise ValueError(f"{name} must be a float32 [B, H, c] tensor")
+    B, H, c = t.shape
+    if c > 1 and t.stride(2) != 1:
+        raise ValueError(f"{name}: rows must be contiguous")
+    if B > 1 and H > 1 and t.stride(0) != H * t.stride(1):
+        raise ValueError(f"{name}: (b, h) vectors must be evenly strided")
+    return t.stride(1) if H > 1 else (t.stride(0) if B > 1 else c)
+
+
+def bwd_delta(o: torch.Tensor, dout: torch.Tensor, out=None) -> torch.Tensor:
+    """Backward row term D = sum over the last dim of O * dO, as float32 of shape o.shape[:-1].
+
+    o, dout: contiguous GPU tensors of one shape, bfloat16 or float32 each.
+    """
+    _gpu(o, dout)
+    if o.shape != dout.shape or not (o.is_contiguous() and dout.is_contiguous()):
+        raise ValueError("o and dout must be contiguous and of one shape")
+    d = o.shape[-1]
+    rows = o.numel() // d if d else 0
+    if out is None:
+        out = torch.empty(o.shape[:-1], dtype=torch.float32, device=o.device)
+    elif out.shape != o.shape[:-1] or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor of shape o.shape[:-1]")
+    with torch.cuda.device(o.device):
+        _raise(lib().ra_bwd_delta(_ptr(o), _dtype_code(o.dtype), _ptr(dout), _dtype_code(dout.dtype), rows, d,
+                                  _ptr(out), _vp(_stream(o.device))), "ra_bwd_delta")
+    return out
+
+
+def backward_round(q_blk, k_blk, v_blk, dout_blk, lse_blk, delta_blk, P: int, p: int, kv: int,
+                   layout="contiguous", causal=True, scale: float = 0.0, grads=None):
+    """Backward of one ring round: device p's query block against K/V block kv.
+
+    q_blk, dout_blk: [B, H, c, d] views with one (b, h) stride; k_blk, v_blk: [B, H, c, d]
+    views; lse_blk, delta_blk: float32 [B, H, c] views (lse: the rows' final log-sum-exp).
+    grads: None or (dq_acc, dk_acc, dv_acc), contiguous float32 [B, H, c, d] accumulators that
+    the pair's contributions are added to (new zeroed ones when None).  Returns the three.
+    """
+    dev = _gpu(q_blk, k_blk, v_blk, dout_blk, lse_blk, delta_blk)
+    B, H, c, d = q_blk.shape
+    for t in (k_blk, v_blk, dout_blk):
+        if t.shape != q_blk.shape or t.dtype != q_blk.dtype:
+            raise ValueError("q, k, v and dout blocks must share a shape and dtype")
+    sq = _block_strides(q_blk, "q")
+    if _block_strides(dout_blk, "dout") != sq:
+        raise ValueError("q and dout must have the same (b, h) stride")
+    sk = _block_strides(k_blk, "k")
+    if _block_strides(v_blk, "v") != sk:
+        raise ValueError("k and v must have the same (b, h) stride")
+    sr = _row_stride(lse_blk, "lse")
+    if _row_stride(delta_blk, "delta") != sr or lse_blk.shape != (B, H, c) or delta_blk.shape != (B, H, c):
+        raise ValueError("lse and delta must be [B, H, c] with the same (b, h) stride")
+    if grads is None:
+        grads = tuple(torch.zeros((B, H, c, d), dtype=torch.float32, device=dev) for _ in range(3))
+    for g in grads:
+        if g.shape != (B, H, c, d) or g.dtype != torch.float32 or not g.is_contiguous():
+            raise ValueError("gradient accumulators must be contiguous float32 [B, H, c, d]")
+    _gpu(q_blk, *grads)
+    pr = _problem(B, H, c * P, d, P, _dtype_code(q_blk.dtype), layout, causal, scale)
+    with torch.cuda.device(dev):
+        _raise(lib().ra_backward_round(ctypes.byref(pr), _ptr(q_blk), _ptr(k_blk), _ptr(v_blk), _ptr(dout_blk),
+                                       _ptr(lse_blk), _ptr(delta_blk), sq, sk, sr, int(p), int(kv),
+                                       _ptr(grads[0]), _ptr(grads[1]), _ptr(grads[2]), _vp(_stream(dev))),
+               "ra_backward_round")
+    return grads
+
+
+def backward(q, k, v, dout, lse, P: int, layout="contiguous", causal=True, p_begin: int = 0,
+             p_end=None, delta=None, o=None, scale: float = 0.0, out=None):
+    """Gradients of forward(q, k, v, ...) for devices [p_begin, p_end), all rounds fused.
+
+    q, k, v: contiguous [B, H, n, d] in layout order; dout: [B, H, m, d], m = (p_end-p_begin)*c,
+    same dtype as q; lse: float32 [B, H, m] from forward; delta: float32 [B, H, m] from
+    bwd_delta, or None with o (forward's output) given to compute it.  Returns float32
+    (dq [B, H, m, d], dk [B, H, n, d], dv [B, H, n, d]); dk and dv hold what the queries of
+    the device range send to every key.
+    """
+    dev = _gpu(q, k, v, dout, lse)
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must be [B, H, n, d] of one shape")
+    if not all(t.is_contiguous() for t in (q, k, v, dout, lse)):
+        raise ValueError("q, k, v, dout and lse must be contiguous")
+    if not (q.dtype == k.dtype == v.dtype == dout.dtype):
+        raise ValueError("q, k, v and dout must share a dtype")
+    B, H, n, d = q.shape
+    p_end = P if p_end is None else p_end
+    c = n // P if P > 0 else 0
+    m = max(0, p_end - p_begin) * c
+    if dout.shape != (B, H, m, d) or lse.shape != (B, H, m) or lse.dtype != torch.float32:
+        raise ValueError(f"dout must be [B, H, {m}, d] and lse float32 [B, H, {m}]")
+    if delta is None:
+        if o is None:
+            raise ValueError("pass delta, or o to compute it")
+        delta = bwd_delta(o, dout)
+    if delta.shape != (B, H, m) or delta.dtype != torch.float32 or not delta.is_contiguous():
+        raise ValueError(f"delta must be contiguous float32 [B, H, {m}]")
+    if out is None:
+        dq = torch.empty((B, H, m, d), dtype=torch.float32, device=dev)
+        dk = torch.empty((B, H, n, d), dtype=torch.float32, device=dev)
+        dv = torch.empty((B, H, n, d), dtype=torch.float32, device=dev)
+    else:
+        dq, dk, dv = out
+    _gpu(q, dq, dk, dv, delta)
+    pr = _problem(B, H, n, d, P, _dtype_code(q.dtype), layout, causal, scale)
+    with torch.cuda.device(dev):
+        _raise(lib().ra_backward(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(delta),
+                                 int(p_begin), int(p_end), _ptr(dq), _ptr(dk), _ptr(dv), _vp(_stream(dev))),
+               "ra_backward")
+    return dq, dk, dv

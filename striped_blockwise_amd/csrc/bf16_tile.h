@@ -1,0 +1,150 @@
+// Building blocks shared by the bf16 attention kernels (head dim 128, gfx950 matrix cores).
+//
+//  * v_mfma_f32_32x32x16_bf16 operand layouts: A (32 rows x 16 contraction) -- lane l holds
+//    row l % 32, contraction elements 8 (l / 32) .. +7; B (16 contraction x 32 columns) -- lane
+//    l holds column l % 32, the same contraction elements; C (32 x 32 fp32) -- lane l holds
+//    column l % 32, rows acc_row(r, l / 32) for r = 0..15.
+//  * A C tile can feed the next MFMA as its B operand directly (column stays in the lane): its
+//    rows become the contraction index in the order acc_row gives them, and the A operand of
+//    that MFMA is then read with the same order (the transposed reads below do that).
+//  * Tiles of 128-element bf16 rows (256 B) live in LDS with each row's sixteen 16-byte chunks
+//    permuted by an XOR mask of the row; HBM -> LDS moves are direct DMA (buffer_load ... lds).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+namespace bf16t {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int D = 128;          // head dim
+constexpr int ROWB = D * 2;     // bytes per row of a tile
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+// Row (within a 32-row MFMA block) held by accumulator register r in lane half h.
+__device__ __forceinline__ int acc_row(int r, int h) { return (r >> 2) * 8 + h * 4 + (r & 3); }
+
+// Swizzle masks (XOR on the 16-byte chunk index of a row).
+//  k_swz: for tiles read only row-wise as A operands (32 consecutive rows, one chunk): any 16
+//         consecutive rows fall on 16 different chunks.
+//  v_swz: for tiles read only with ds_read_b64_tr_b16, where one 32-lane half reads 4
+//         consecutive rows x 4 consecutive chunks (8 B per lane): bits {0b1010 for row bit 0,
+//         0b0100 for row bit 1} put those 16 (row, chunk) pairs on 16 different chunks and any
+//         16 lanes on 8 different chunk pairs.
+//  t_swz: for tiles read both ways: v_swz, whose four values on an aligned group of 4 rows keep
+//         the transposed reads conflict-free, XORed with a per-group term {0, 1, 8, 9} (constant
+//         within the group) that makes any 16 aligned rows take 16 different masks and any 8
+//         aligned rows 8 different values of mask & 7, as the row-wise reads need.
+__device__ __forceinline__ int k_swz(int row) { return row & 15; }
+__device__ __forceinline__ int v_swz(int row) { return ((row & 1) ? 10 : 0) ^ ((row & 2) ? 4 : 0); }
+__device__ __forceinline__ int t_swz(int row) {
+  return v_swz(row) ^ ((row & 4) ? 1 : 0) ^ ((row & 8) ? 8 : 0);
+}
+enum Swz { SWZ_K = 0, SWZ_V = 1, SWZ_T = 2 };
+template <int S>
+__device__ __forceinline__ int swz(int row) {
+  return S == SWZ_K ? k_swz(row) : (S == SWZ_V ? v_swz(row) : t_swz(row));
+}
+template <int S>
+__device__ __forceinline__ int tile_off(int row, int byte_in_row) {
+  return row * ROWB + ((((byte_in_row >> 4) ^ swz<S>(row))) << 4) + (byte_in_row & 15);
+}
+
+__device__ __forceinline__ float pair_max(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+// LDS offset (relative to a tile) of lane `lane`'s row-wise A-operand read of contraction step
+// dk (16 elements) for 32-row block 0: row l % 32, elements 16 dk + 8 (l / 32) .. +7.
+template <int S>
+__device__ __forceinline__ int a_rowwise_off(int lane, int dk) {
+  return tile_off<S>(lane & 31, (2 * dk + (lane >> 5)) * 16);
+}
+
+// LDS offsets of the transposed A-operand reads (ds_read_b64_tr_b16) for column block db (32
+// columns of the tile, i.e. 32 consecutive head-dim elements) and half `sec` of a 16-row
+// contraction step.  In each 16-lane group, result lane 4a+b element e comes from element b of
+// source lane 4e+a; source lane (G, e, a) therefore points at row 4 h + e (+8 for sec = 1),
+// h = G / 2, elements 32 db + 16 (G % 2) + 4 a .. +3, so that result lane L holds column
+// 32 db + L % 32 and rows {4h..4h+3} / {8+4h..8+4h+3} -- the rows acc_row gives lane half h.
+template <int S>
+__device__ __forceinline__ int a_tr_off(int lane, int db, int sec) {
+  const int G = lane >> 4, e = (lane >> 2) & 3, aa = lane & 3;
+  const int h = G >> 1, g2 = G & 1;
+  const int row = 4 * h + e + 8 * sec;
+  const int d = 32 * db + 16 * g2 + 4 * aa;
+  return tile_off<S>(row, 2 * d);
+}
+
+// Transposed A operand (rows of the tile become the contraction index): 16 tile rows starting
+// at byte offset `rows_off` within the tile, column block db.
+__device__ __forceinline__ bf16x8 read_a_tr(const char* tile, int off_lo, int off_hi) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off_lo));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off_hi));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// DMA of tiles of ROWS rows (row-major, 256 B per row) into LDS, split into 1 KB segments (4
+// rows) over NW wavefronts: wave w does segments w, w + NW, ...  Each wave keeps the per-lane
+// offsets of its segments in `unsigned voff[DmaShape<NW, ROWS>::PER_WAVE]`: lane j of segment
+// seg fills LDS row 4 seg + j / 16 at physical chunk j % 16, which holds logical chunk
+// (j % 16) ^ mask(row) of that row (the XOR permutation is its own inverse).  The offsets pass as
+// plain pointers: with an array reference, or a struct holding the array, hipcc's host pass
+// reported a substitution failure for these device templates (or, for member functions, quietly
+// dropped the launch stub of every kernel instantiation after the first).
+template <int NW, int ROWS>
+struct DmaShape {
+  static constexpr int SEGS = ROWS * ROWB / 1024;
+  static constexpr int PER_WAVE = (SEGS + NW - 1) / NW;
+};
+
+template <int NW, int ROWS>
+__device__ __forceinline__ void dma_init(unsigned* voff, Swz kind, int wave_u, int lane) {
+#pragma unroll
+  for (int i = 0; i < DmaShape<NW, ROWS>::PER_WAVE; ++i) {
+    const int row = (wave_u + i * NW) * 4 + (lane >> 4);
+    const int mask = kind == SWZ_K ? swz<SWZ_K>(row) : (kind == SWZ_V ? swz<SWZ_V>(row) : swz<SWZ_T>(row));
+    voff[i] = (unsigned)(row * ROWB + (((lane & 15) ^ mask) << 4));
+  }
+}
+
+// Rows x0 .. x0 + ROWS - 1 of a block of c rows at `block` into the LDS tile `tile`.  The buffer
+// descriptor starts at row x0 and holds only the rows that exist, so the per-lane offsets are
+// loop constants and rows past the end of the block are out of range: the buffer unit returns
+// zeros for them, which land in LDS.
+template <int NW, int ROWS>
+__device__ __forceinline__ void dma_issue(const unsigned* voff, const char* block, char* tile, int x0, int c,
+                                          int wave_u) {
+  constexpr int SEGS = DmaShape<NW, ROWS>::SEGS;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(block + (int64_t)x0 * ROWB), 0, (c - x0) * ROWB, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < DmaShape<NW, ROWS>::PER_WAVE; ++i) {
+    const int seg = wave_u + i * NW;
+    if (SEGS % NW == 0 || seg < SEGS)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + seg * 1024), 16, voff[i], 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_dma_and_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's LDS DMA has landed
+  __syncthreads();
+}
+
+}  // namespace bf16t
+}  // namespace ra

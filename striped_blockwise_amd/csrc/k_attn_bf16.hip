@@ -23,22 +23,14 @@
 // way because O, l and the reference max always stay consistent.
 #include <type_traits>
 
+#include "bf16_tile.h"
 #include "ra_internal.h"
 
 namespace ra {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+using namespace bf16t;
 
-constexpr int D = 128;          // head dim
-constexpr int ROWB = D * 2;     // bytes per K / V row
 #ifndef RA_BF16_NW
 #define RA_BF16_NW 4            // wavefronts per workgroup
 #endif
@@ -47,8 +39,6 @@ constexpr int ROWB = D * 2;     // bytes per K / V row
 #endif
 constexpr int NW = RA_BF16_NW;  // wavefronts per workgroup
 constexpr int NT = NW * 64;     // threads per workgroup
-constexpr float LOG2E = 1.4426950408889634f;
-constexpr float LN2 = 0.6931471805599453f;
 constexpr float TAU = 8.0f;     // lazy-rescale threshold, log2 units
 
 #ifndef RA_BF16_QB
@@ -61,32 +51,9 @@ constexpr float TAU = 8.0f;     // lazy-rescale threshold, log2 units
 #define RA_BF16_OCC 2           // target wavefronts per SIMD
 #endif
 
-// LDS layout of a K or V tile: row = key, 256 B = 16 chunks of 16 B, each row's chunks permuted
-// by an XOR with a per-row mask.  K tiles are read as MFMA A operands (32 consecutive rows, one
-// chunk): mask = row & 15 puts any 16 consecutive rows on 16 different chunks.  V tiles are read
-// with ds_read_b64_tr_b16, where one 32-lane half reads 4 consecutive rows x 4 consecutive
-// chunks (8 B per lane): mask bits {0b1010 for row bit 0, 0b0100 for row bit 1} make those 16
-// (row, chunk) pairs land on 16 different chunks, and any 16 lanes on 8 different chunk pairs.
-__device__ __forceinline__ int k_swz(int row) { return row & 15; }
-__device__ __forceinline__ int v_swz(int row) { return ((row & 1) ? 10 : 0) ^ ((row & 2) ? 4 : 0); }
-__device__ __forceinline__ int k_off(int row, int byte_in_row) {
-  return row * ROWB + ((((byte_in_row >> 4) ^ k_swz(row))) << 4) + (byte_in_row & 15);
-}
-__device__ __forceinline__ int v_off(int row, int byte_in_row) {
-  return row * ROWB + ((((byte_in_row >> 4) ^ v_swz(row))) << 4) + (byte_in_row & 15);
-}
-
-__device__ __forceinline__ float pair_max(float x) {
-  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
-}
-
-// Key index (within a 32-key MFMA block) held by accumulator register r in lane half h.
-__device__ __forceinline__ int acc_row(int r, int h) { return (r >> 2) * 8 + h * 4 + (r & 3); }
+// LDS layout of a K or V tile: row = key, 256 B = 16 chunks of 16 B with a per-row XOR mask on
+// the chunk index.  K tiles are only read row-wise (MFMA A operand), V tiles only transposed
+// (ds_read_b64_tr_b16), so each gets the mask that is conflict-free for its own read pattern.
 
 template <int QB, int TK, bool STATS>
 struct Attn {
@@ -95,69 +62,20 @@ struct Attn {
   static constexpr int KB = TK / 32;              // 32-key MFMA blocks per tile
   static constexpr int KS = TK / 16;              // 16-key MFMA k-steps per tile (P V)
   static constexpr int TILE = TK * ROWB;          // bytes of one K or V tile
-  static constexpr int DMA_SEGS = TILE / 1024;                        // 1 KB wave-wide DMAs per tile
-  static constexpr int DMA_PER_WAVE = (DMA_SEGS + NW - 1) / NW;       // segments wave w: w, w+NW, ...
 
   // Per-lane constant parts of the LDS addresses.
   int k_base[8];       // K operand: row l32, chunk (2 dk + hh)
   int v_base[4][2];    // V^T operand: transposed reads, [d-block][first/second 4 keys]
 
   __device__ __forceinline__ void init_offsets(int lane) {
-    const int l32 = lane & 31, hh = lane >> 5;
 #pragma unroll
-    for (int dk = 0; dk < 8; ++dk) k_base[dk] = k_off(l32, (2 * dk + hh) * 16);
-    // ds_read_b64_tr_b16: in each 16-lane group, result lane 4a+b element e comes from element b
-    // of source lane 4e+a.  Source lane (G, e, a) therefore points at V[key(G, e)][d(G, a)..+3]
-    // with key = 4 h + e (+8 for the second read), h = G / 2, and d = 16 (G % 2) + 4 a, so that
-    // result lane L holds d = 32 db + L % 32 and keys {4h..4h+3} / {8+4h..8+4h+3}.
-    const int G = lane >> 4, e = (lane >> 2) & 3, aa = lane & 3;
-    const int h = G >> 1, g2 = G & 1;
+    for (int dk = 0; dk < 8; ++dk) k_base[dk] = a_rowwise_off<SWZ_K>(lane, dk);
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int sec = 0; sec < 2; ++sec) {
-        const int key = 4 * h + e + 8 * sec;
-        const int d = 32 * db + 16 * g2 + 4 * aa;
-        v_base[db][sec] = v_off(key, 2 * d);
-      }
+      for (int sec = 0; sec < 2; ++sec) v_base[db][sec] = a_tr_off<SWZ_V>(lane, db, sec);
   }
 };
-
-// DMA one K or V tile (keys x0 .. x0+TK-1 of a block of c rows at `block`) into an LDS stage.
-// The buffer descriptor starts at row x0 and holds only the rows that exist, so the per-lane
-// offsets are loop constants and rows past the end of the block are out of range: the buffer
-// unit returns zeros for them, which land in LDS (zero keys are masked out of the scores, and
-// zero values contribute nothing).
-template <int DMA_PER_WAVE, int DMA_SEGS>
-__device__ __forceinline__ void dma_tile(const char* block, char* stage, int x0, int c,
-                                         const unsigned* voff, int wave_u) {
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(block + (int64_t)x0 * ROWB), 0, (c - x0) * ROWB, 0x00020000);
-#pragma unroll
-  for (int i = 0; i < DMA_PER_WAVE; ++i) {
-    const int seg = wave_u + i * NW;                      // 1 KB segment = 4 rows
-    if (DMA_SEGS % NW == 0 || seg < DMA_SEGS)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(stage + seg * 1024), 16, voff[i], 0, 0, 0);
-  }
-}
-
-// Per-lane byte offsets (relative to the tile's first row) of a wave's DMA segments: lane j of
-// segment seg fills LDS row 4 seg + j / 16 at physical chunk j % 16, which holds logical chunk
-// (j % 16) ^ mask(row) of that row (the XOR permutation is its own inverse).
-template <int DMA_PER_WAVE, bool IS_V>
-__device__ __forceinline__ void dma_offsets(unsigned* voff, int wave_u, int lane) {
-#pragma unroll
-  for (int i = 0; i < DMA_PER_WAVE; ++i) {
-    const int row = (wave_u + i * NW) * 4 + (lane >> 4);
-    const int mask = IS_V ? v_swz(row) : k_swz(row);
-    voff[i] = (unsigned)(row * ROWB + (((lane & 15) ^ mask) << 4));
-  }
-}
-
-__device__ __forceinline__ void wait_dma_and_barrier() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's LDS DMA has landed
-  __syncthreads();
-}
 
 template <int QB, int TK, bool STATS>
 __global__ __launch_bounds__(NT, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) {
@@ -201,9 +119,9 @@ __global__ __launch_bounds__(NT, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) {
 
   A off;
   off.init_offsets(lane);
-  unsigned dko[A::DMA_PER_WAVE], dvo[A::DMA_PER_WAVE];
-  dma_offsets<A::DMA_PER_WAVE, false>(dko, wave_u, lane);
-  dma_offsets<A::DMA_PER_WAVE, true>(dvo, wave_u, lane);
+  unsigned kdma[DmaShape<NW, TK>::PER_WAVE], vdma[DmaShape<NW, TK>::PER_WAVE];
+  dma_init<NW, TK>(kdma, SWZ_K, wave_u, lane);
+  dma_init<NW, TK>(vdma, SWZ_V, wave_u, lane);
 
   // ---- Q columns (B operand): lane holds row qw0 + 32 qb + l32, head dims 16 dk + 8 hh .. +7
   const __bf16* qp = (const __bf16*)a.q + bh * a.q_bh_stride + dev * a.q_dev_stride;
@@ -309,9 +227,7 @@ __global__ __launch_bounds__(NT, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) {
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vs_ + off.v_base[db][0] + ks * 16 * ROWB));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vs_ + off.v_base[db][1] + ks * 16 * ROWB));
-        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 va = read_a_tr(vs_ + ks * 16 * ROWB, off.v_base[db][0], off.v_base[db][1]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[qb][ks], o[qb][db], 0, 0, 0);
@@ -372,14 +288,14 @@ __global__ __launch_bounds__(NT, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) {
     if (ntk > 0) {
       // tile t lives in stage t & 1; its DMA was issued one iteration earlier.  The loop is
       // unrolled by two so that the stage offsets are compile-time immediates.
-      dma_tile<A::DMA_PER_WAVE, A::DMA_SEGS>(kblk, kst(0), 0, c, dko, wave_u);
-      dma_tile<A::DMA_PER_WAVE, A::DMA_SEGS>(vblk, vst(0), 0, c, dvo, wave_u);
+      dma_issue<NW, TK>(kdma, kblk, kst(0), 0, c, wave_u);
+      dma_issue<NW, TK>(vdma, vblk, vst(0), 0, c, wave_u);
       auto iter = [&](int t, auto stage_c) __attribute__((always_inline)) {
         constexpr int S = decltype(stage_c)::value;
         wait_dma_and_barrier();                       // tile t landed; the other stage is free
         if (t + 1 < ntk) {
-          dma_tile<A::DMA_PER_WAVE, A::DMA_SEGS>(kblk, smem + (1 - S) * TILE, (t + 1) * TK, c, dko, wave_u);
-          dma_tile<A::DMA_PER_WAVE, A::DMA_SEGS>(vblk, smem + (3 - S) * TILE, (t + 1) * TK, c, dvo, wave_u);
+          dma_issue<NW, TK>(kdma, kblk, smem + (1 - S) * TILE, (t + 1) * TK, c, wave_u);
+          dma_issue<NW, TK>(vdma, vblk, smem + (3 - S) * TILE, (t + 1) * TK, c, wave_u);
         }
         const int cls = tile_class(t);
         if (cls) {

@@ -1,0 +1,449 @@
+// bf16 backward of blockwise attention on gfx950 matrix cores (v_mfma_f32_32x32x16_bf16), head
+// dim 128.
+//
+// The pages give only the forward; its gradients follow from O = softmax(S + C) V with
+// S = Q K^T * scale (Striped Attention review, "核心公式"; Ring Attention review, step 3).  With
+// the forward's log-sum-exp L of each query row, a (query block, K/V block) pair has the exact
+// probabilities P = exp(S + C - L) on its own, so the ring's rounds are independent and each
+// pair contributes
+//     dV += P^T dO,   dP = dO V^T,   dS = P * (dP - D),   dQ += scale dS K,   dK += scale dS^T Q,
+// with D = rowsum(O * dO).  The same GetMask classes as the forward decide which pairs count
+// (Striped Attention review, "GetMask 函数") and which tiles are skipped or run unmasked.
+//
+// Two kernels, neither with atomics, so every gradient is a deterministic sum:
+//   dQ kernel   query rows stationary (32 per wavefront), the K/V tiles of the given rounds
+//               streamed through LDS as in the forward:
+//                 S^T = K Q^T, dP^T = V dO^T (A = K / V rows from LDS, B = Q / dO in registers),
+//                 dS^T = P^T * (dP^T - D) in registers (one query per lane),
+//                 dQ^T += K^T dS^T (A = K read transposed from the same LDS tile).
+//   dK/dV kernel key rows stationary (32 per wavefront), the query tiles of every device that
+//               meets the block streamed through LDS (Q, dO, L, D):
+//                 S = Q K^T, dP = dO V^T (A = Q / dO rows from LDS, B = K / V in registers),
+//                 dS = P * (dP - D) in registers (one key per lane),
+//                 dV^T += dO^T P, dK^T += Q^T dS (A = dO / Q read transposed).
+// A tile read both row-wise and transposed uses the t_swz chunk mask, conflict-free for both.
+// Rows past the end of a block arrive in LDS as zeros: a zero query row with L = D = 0 gives
+// P = 1 and dS = 0 and adds nothing; zero key rows are masked in the dQ kernel and only reach
+// their own (unwritten) dK/dV columns in the dK/dV kernel.
+#include <type_traits>
+
+#include "bf16_tile.h"
+#include "ra_internal.h"
+
+namespace ra {
+namespace {
+
+using namespace bf16t;
+
+constexpr int NW = 4;            // wavefronts per workgroup
+constexpr int NT = NW * 64;
+constexpr int WR = 32;           // stationary rows per wavefront
+constexpr int WG_ROWS = NW * WR; // stationary rows per workgroup
+constexpr int TS = 32;           // streamed rows per tile
+constexpr int TILE = TS * ROWB;  // bytes of one streamed tile (8 KB)
+constexpr float NEG_BIG = -1e30f;  // clamp for L = -inf (a row that sees no key): P stays 0
+
+// Block -> (stream, tile).  Blocks are dispatched round-robin over the 8 XCDs; with xcd_major
+// XCD x takes streams x, x+8, ... one after another, all tiles of a stream together, so the
+// workgroups on one XCD share the streamed blocks in its L2.  `reverse` puts the last tile
+// first (dQ: late query rows see the most keys; dK/dV: early key rows meet the most queries).
+__device__ __forceinline__ void map_block(int xcd_major, int nstream, int ntile, bool reverse,
+                                          int& stream, int& tile) {
+  if (xcd_major) {
+    const int x = blockIdx.x & 7;
+    const int sq = blockIdx.x >> 3;
+    stream = (sq / ntile) * 8 + x;
+    tile = sq % ntile;
+  } else {
+    stream = blockIdx.x % nstream;
+    tile = blockIdx.x / nstream;
+  }
+  if (reverse) tile = ntile - 1 - tile;
+}
+
+__device__ __forceinline__ bf16x8 load_row8(const __bf16* p, bool ok) {
+  return ok ? *reinterpret_cast<const bf16x8*>(p) : bf16x8{};
+}
+
+// Packs f(r) for r = 8 ks .. 8 ks + 7 into bf16 (round to nearest even): the B operand of
+// contraction step ks.
+template <typename F>
+__device__ __forceinline__ bf16x8 pack8(F&& f, int ks) {
+  bf16x8 out;
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const bf16x2 pp = __builtin_convertvector(f32x2{f(8 * ks + e), f(8 * ks + e + 1)}, bf16x2);
+    out[e] = pp[0];
+    out[e + 1] = pp[1];
+  }
+  return out;
+}
+
+// Writes (or adds) acc * mul for the lane's stationary row: rows d = 32 db + acc_row(r, h).
+__device__ __forceinline__ void store_rows(float* row, const f32x16 (&acc)[4], float mul, int hh, bool add) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float4* dst = reinterpret_cast<float4*>(row + 32 * db + 8 * g + 4 * hh);
+      float4 w = make_float4(acc[db][4 * g] * mul, acc[db][4 * g + 1] * mul, acc[db][4 * g + 2] * mul,
+                             acc[db][4 * g + 3] * mul);
+      if (add) {
+        const float4 o = *dst;
+        w.x += o.x; w.y += o.y; w.z += o.z; w.w += o.w;
+      }
+      *dst = w;
+    }
+}
+
+// ------------------------------------------------------------------------------- dQ kernel
+__global__ __launch_bounds__(NT, 2) void k_bwd_dq_bf16(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];   // K0 K1 V0 V1
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int c = a.c;
+
+  const int nqt = (c + WG_ROWS - 1) / WG_ROWS;
+  int stream, qt;
+  map_block(a.xcd_major, a.BH * a.n_dev, nqt, true, stream, qt);
+  const int bh = stream % a.BH;
+  const int dev = stream / a.BH;
+  const int p = a.p_begin + dev;
+  const int q_wg_last = min(c, qt * WG_ROWS + WG_ROWS) - 1;
+  const int qw0 = qt * WG_ROWS + wave_u * WR;
+  const int qw_last = min(c, qw0 + WR) - 1;
+  const bool wave_live = qw0 < c;
+  const int y = qw0 + l32;
+
+  int k_row[8], v_row[8], k_tr[4][2];
+#pragma unroll
+  for (int dk = 0; dk < 8; ++dk) {
+    k_row[dk] = a_rowwise_off<SWZ_T>(lane, dk);
+    v_row[dk] = a_rowwise_off<SWZ_K>(lane, dk);
+  }
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec) k_tr[db][sec] = a_tr_off<SWZ_T>(lane, db, sec);
+  unsigned kdma[DmaShape<NW, TS>::PER_WAVE], vdma[DmaShape<NW, TS>::PER_WAVE];
+  dma_init<NW, TS>(kdma, SWZ_T, wave_u, lane);
+  dma_init<NW, TS>(vdma, SWZ_K, wave_u, lane);
+
+  // B operands: this lane's query row of Q and dO, head dims 16 dk + 8 hh .. +7
+  const __bf16* qp = (const __bf16*)a.q + bh * a.q_bh_stride + dev * a.q_dev_stride + (int64_t)y * D + hh * 8;
+  const __bf16* dop = (const __bf16*)a.dout + bh * a.do_bh_stride + dev * a.do_dev_stride + (int64_t)y * D + hh * 8;
+  bf16x8 qf[8], df[8];
+#pragma unroll
+  for (int dk = 0; dk < 8; ++dk) {
+    qf[dk] = load_row8(qp + dk * 16, y < c);
+    df[dk] = load_row8(dop + dk * 16, y < c);
+  }
+  float nl = 0.f, dl = 0.f;    // -L log2(e) and D of this lane's row
+  if (y < c) {
+    const int64_t ro = bh * a.row_bh_stride + dev * a.row_dev_stride + y;
+    nl = -fmaxf(a.lse[ro], NEG_BIG) * LOG2E;
+    dl = a.delta[ro];
+  }
+  const float cs = a.scale * LOG2E;
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) acc[db] = f32x16{};
+
+  const int ntk_all = (c + TS - 1) / TS;
+  for (int rr = 0; rr < a.r_count; ++rr) {
+    const int r = a.r_begin + rr;
+    const int k = ring_block(p, r, a.P);
+    const int mode = round_mode(a.layout, a.causal, p, k);
+    const int delta = mode == MODE_STRICT ? 1 : 0;
+    int ntk = ntk_all;
+    if (mode == MODE_SKIP) ntk = 0;
+    else if (mode != MODE_FULL) ntk = (q_wg_last - delta < 0) ? 0 : min(ntk_all, (q_wg_last - delta) / TS + 1);
+    if (ntk == 0) continue;
+
+    const int64_t kvo = bh * a.kv_bh_stride + (int64_t)(k - a.kv_base) * a.kv_blk_stride;
+    const char* kblk = (const char*)((const __bf16*)a.k + kvo);
+    const char* vblk = (const char*)((const __bf16*)a.v + kvo);
+
+    // 0: no visible pair for this wave; 1: all visible; 2: element mask (diagonal, or the
+    // tile runs past the end of the block)
+    auto tile_class = [&](int t) -> int {
+      const int x0 = t * TS;
+      if (!wave_live || (mode != MODE_FULL && x0 > qw_last - delta)) return 0;
+      const bool full = (mode == MODE_FULL || x0 + TS - 1 <= qw0 - delta) && x0 + TS <= c;
+      return full ? 1 : 2;
+    };
+
+    auto compute = [&](const char* ks_, const char* vs_, int t, bool masked) __attribute__((always_inline)) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+      {
+        bf16x8 kf[8];
+#pragma unroll
+        for (int dk = 0; dk < 8; ++dk) kf[dk] = *reinterpret_cast<const bf16x8*>(ks_ + k_row[dk]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int dk = 0; dk < 8; ++dk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[dk], qf[dk], s, 0, 0, 0);
+      }
+      {
+        bf16x8 vf[8];
+#pragma unroll
+        for (int dk = 0; dk < 8; ++dk) vf[dk] = *reinterpret_cast<const bf16x8*>(vs_ + v_row[dk]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int dk = 0; dk < 8; ++dk) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dk], df[dk], dp, 0, 0, 0);
+      }
+      if (masked) {
+        const int x0 = t * TS;
+#pragma unroll
+        for (int rg = 0; rg < 16; ++rg) {
+          const int x = x0 + acc_row(rg, hh);
+          const bool vis = x < c && (mode == MODE_FULL || x <= y - delta);
+          s[rg] = vis ? s[rg] : -INFINITY;
+        }
+      }
+      auto ds = [&](int rg) __attribute__((always_inline)) {
+        const float pr = __builtin_amdgcn_exp2f(fmaf(s[rg], cs, nl));
+        return pr * (dp[rg] - dl);
+      };
+      const bf16x8 ds0 = pack8(ds, 0);
+      const bf16x8 ds1 = pack8(ds, 1);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16x8 k0 = read_a_tr(ks_, k_tr[db][0], k_tr[db][1]);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, ds0, acc[db], 0, 0, 0);
+        const bf16x8 k1 = read_a_tr(ks_ + 16 * ROWB, k_tr[db][0], k_tr[db][1]);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, ds1, acc[db], 0, 0, 0);
+      }
+    };
+
+    dma_issue<NW, TS>(kdma, kblk, smem, 0, c, wave_u);
+    dma_issue<NW, TS>(vdma, vblk, smem + 2 * TILE, 0, c, wave_u);
+    auto iter = [&](int t, auto stage_c) __attribute__((always_inline)) {
+      constexpr int S = decltype(stage_c)::value;
+      wait_dma_and_barrier();                         // tile t landed; the other stage is free
+      if (t + 1 < ntk) {
+        dma_issue<NW, TS>(kdma, kblk, smem + (1 - S) * TILE, (t + 1) * TS, c, wave_u);
+        dma_issue<NW, TS>(vdma, vblk, smem + (3 - S) * TILE, (t + 1) * TS, c, wave_u);
+      }
+      const int cls = tile_class(t);
+      if (cls) compute(smem + S * TILE, smem + (2 + S) * TILE, t, cls == 2);
+    };
+    int t = 0;
+    for (; t + 1 < ntk; t += 2) {
+      iter(t, std::integral_constant<int, 0>{});
+      iter(t + 1, std::integral_constant<int, 1>{});
+    }
+    if (t < ntk) iter(t, std::integral_constant<int, 0>{});
+    __syncthreads();                                  // LDS stages free for the next round
+  }
+
+  if (y < c)
+    store_rows(a.dq + bh * a.dq_bh_stride + ((int64_t)dev * c + y) * D, acc, a.scale, hh, a.accumulate != 0);
+}
+
+// ---------------------------------------------------------------------------- dK/dV kernel
+// LDS per stage: Q tile, dO tile, then 32 floats of L and 32 of D.
+constexpr int RS_BYTES = 2 * TS * 4;
+
+__global__ __launch_bounds__(NT, 1) void k_bwd_dkv_bf16(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE + 2 * RS_BYTES];  // Q0 Q1 O0 O1 RS0 RS1
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int c = a.c;
+
+  const int nkt = (c + WG_ROWS - 1) / WG_ROWS;
+  int stream, kt;
+  map_block(a.xcd_major, a.BH * a.n_kv, nkt, false, stream, kt);
+  const int bh = stream % a.BH;
+  const int kvi = stream / a.BH;
+  const int kblk = a.kv_base + kvi;
+  const int x_wg0 = kt * WG_ROWS;
+  const int kw0 = x_wg0 + wave_u * WR;
+  const int kw_last = min(c, kw0 + WR) - 1;
+  const bool wave_live = kw0 < c;
+  const int x = kw0 + l32;
+
+  int q_row[8], q_tr[4][2];
+#pragma unroll
+  for (int dk = 0; dk < 8; ++dk) q_row[dk] = a_rowwise_off<SWZ_T>(lane, dk);
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec) q_tr[db][sec] = a_tr_off<SWZ_T>(lane, db, sec);
+  unsigned dma[DmaShape<NW, TS>::PER_WAVE];
+  dma_init<NW, TS>(dma, SWZ_T, wave_u, lane);
+
+  // B operands: this lane's key row of K and V
+  const int64_t kvo = bh * a.kv_bh_stride + (int64_t)kvi * a.kv_blk_stride + (int64_t)x * D + hh * 8;
+  bf16x8 kf[8], vf[8];
+#pragma unroll
+  for (int dk = 0; dk < 8; ++dk) {
+    kf[dk] = load_row8((const __bf16*)a.k + kvo + dk * 16, x < c);
+    vf[dk] = load_row8((const __bf16*)a.v + kvo + dk * 16, x < c);
+  }
+  const float cs = a.scale * LOG2E;
+
+  f32x16 dka[4], dva[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) { dka[db] = f32x16{}; dva[db] = f32x16{}; }
+
+  const int ntq = (c + TS - 1) / TS;
+  for (int di = 0; di < a.n_dev; ++di) {
+    const int p = a.p_begin + di;
+    const int mode = round_mode(a.layout, a.causal, p, kblk);
+    const int delta = mode == MODE_STRICT ? 1 : 0;
+    if (mode == MODE_SKIP) continue;
+    // first query tile holding a row y >= x_wg0 + delta (a visible pair for some key here)
+    const int t0 = mode == MODE_FULL ? 0 : (x_wg0 + delta) / TS;
+    if (t0 >= ntq) continue;
+
+    const char* qblk = (const char*)((const __bf16*)a.q + bh * a.q_bh_stride + di * a.q_dev_stride);
+    const char* oblk = (const char*)((const __bf16*)a.dout + bh * a.do_bh_stride + di * a.do_dev_stride);
+    const float* lblk = a.lse + bh * a.row_bh_stride + di * a.row_dev_stride;
+    const float* dblk = a.delta + bh * a.row_bh_stride + di * a.row_dev_stride;
+
+    auto issue = [&](int t, int S) __attribute__((always_inline)) {
+      const int y0 = t * TS;
+      dma_issue<NW, TS>(dma, qblk, smem + S * TILE, y0, c, wave_u);
+      dma_issue<NW, TS>(dma, oblk, smem + (2 + S) * TILE, y0, c, wave_u);
+      if (wave_u == 0 && lane < 32) {
+        // lane i < 32 copies L and D of row y0 + i to bytes 4 i of the stage's L and D areas;
+        // rows past the block end read as 0
+        char* rs = smem + 4 * TILE + S * RS_BYTES;
+        const unsigned bytes = (unsigned)(c - y0) * 4;
+        const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc((void*)(lblk + y0), 0, bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t dr = __builtin_amdgcn_make_buffer_rsrc((void*)(dblk + y0), 0, bytes, 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(lr, (lds_void*)rs, 4, (unsigned)(lane * 4), 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(dr, (lds_void*)(rs + TS * 4), 4, (unsigned)(lane * 4), 0, 0, 0);
+      }
+    };
+
+    // 0: no visible pair for this wave; 1: all visible; 2: element mask
+    auto tile_class = [&](int t) -> int {
+      const int y0 = t * TS;
+      const int y_last = min(c, y0 + TS) - 1;
+      if (!wave_live || (mode != MODE_FULL && kw0 > y_last - delta)) return 0;
+      return (mode == MODE_FULL || kw_last <= y0 - delta) ? 1 : 2;
+    };
+
+    auto compute = [&](const char* qs_, const char* os_, const char* rs_, int t, bool masked) __attribute__((always_inline)) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+      {
+        bf16x8 qa[8];
+#pragma unroll
+        for (int dk = 0; dk < 8; ++dk) qa[dk] = *reinterpret_cast<const bf16x8*>(qs_ + q_row[dk]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int dk = 0; dk < 8; ++dk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[dk], kf[dk], s, 0, 0, 0);
+      }
+      {
+        bf16x8 oa[8];
+#pragma unroll
+        for (int dk = 0; dk < 8; ++dk) oa[dk] = *reinterpret_cast<const bf16x8*>(os_ + q_row[dk]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int dk = 0; dk < 8; ++dk) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[dk], vf[dk], dp, 0, 0, 0);
+      }
+      if (masked) {
+        const int y0 = t * TS;
+#pragma unroll
+        for (int rg = 0; rg < 16; ++rg) {
+          const int yy = y0 + acc_row(rg, hh);
+          const bool vis = mode == MODE_FULL || x <= yy - delta;
+          s[rg] = vis ? s[rg] : -INFINITY;
+        }
+      }
+      // L and D of rows acc_row(rg, hh): four runs of 4 consecutive rows
+      float pr[16], dsv[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 l4 = *reinterpret_cast<const float4*>(rs_ + (8 * g + 4 * hh) * 4);
+        const float4 d4 = *reinterpret_cast<const float4*>(rs_ + TS * 4 + (8 * g + 4 * hh) * 4);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int rg = 4 * g + j;
+          pr[rg] = __builtin_amdgcn_exp2f(fmaf(s[rg], cs, -fmaxf(lv[j], NEG_BIG) * LOG2E));
+          dsv[rg] = pr[rg] * (dp[rg] - dv[j]);
+        }
+      }
+      const bf16x8 p0 = pack8([&](int r) { return pr[r]; }, 0);
+      const bf16x8 p1 = pack8([&](int r) { return pr[r]; }, 1);
+      const bf16x8 s0 = pack8([&](int r) { return dsv[r]; }, 0);
+      const bf16x8 s1 = pack8([&](int r) { return dsv[r]; }, 1);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16x8 o0 = read_a_tr(os_, q_tr[db][0], q_tr[db][1]);
+        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o0, p0, dva[db], 0, 0, 0);
+        const bf16x8 o1 = read_a_tr(os_ + 16 * ROWB, q_tr[db][0], q_tr[db][1]);
+        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o1, p1, dva[db], 0, 0, 0);
+        const bf16x8 q0 = read_a_tr(qs_, q_tr[db][0], q_tr[db][1]);
+        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q0, s0, dka[db], 0, 0, 0);
+        const bf16x8 q1 = read_a_tr(qs_ + 16 * ROWB, q_tr[db][0], q_tr[db][1]);
+        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q1, s1, dka[db], 0, 0, 0);
+      }
+    };
+
+    issue(t0, 0);
+    auto iter = [&](int t, auto stage_c) __attribute__((always_inline)) {
+      constexpr int S = decltype(stage_c)::value;
+      wait_dma_and_barrier();
+      if (t + 1 < ntq) issue(t + 1, 1 - S);
+      const int cls = tile_class(t);
+      if (cls) compute(smem + S * TILE, smem + (2 + S) * TILE, smem + 4 * TILE + S * RS_BYTES, t, cls == 2);
+    };
+    int t = t0;
+    for (; t + 1 < ntq; t += 2) {
+      iter(t, std::integral_constant<int, 0>{});
+      iter(t + 1, std::integral_constant<int, 1>{});
+    }
+    if (t < ntq) iter(t, std::integral_constant<int, 0>{});
+    __syncthreads();
+  }
+
+  if (x < c) {
+    const int64_t ro = bh * a.dkv_bh_stride + ((int64_t)kvi * c + x) * D;
+    store_rows(a.dk + ro, dka, a.scale, hh, a.accumulate != 0);
+    store_rows(a.dv + ro, dva, 1.0f, hh, a.accumulate != 0);
+  }
+}
+
+}  // namespace
+
+bool bwd_bf16_supported(int64_t d) { return d == D; }
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, int d, bool dq, bool dkv, hipStream_t s) {
+  if (d != D) return hipErrorInvalidValue;
+  const int64_t ntile = (a.c + WG_ROWS - 1) / WG_ROWS;
+  if (dkv) {
+    const int64_t nstream = (int64_t)a.BH * a.n_kv;
+    const int64_t blocks = ntile * nstream;
+    if (blocks * NT >= (1ll << 32)) return hipErrorInvalidConfiguration;
+    BwdArgs b = a;
+    b.xcd_major = nstream % 8 == 0 ? 1 : 0;
+    hipLaunchKernelGGL(k_bwd_dkv_bf16, dim3((unsigned)blocks), dim3(NT), 0, s, b);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (dq) {
+    const int64_t nstream = (int64_t)a.BH * a.n_dev;
+    const int64_t blocks = ntile * nstream;
+    if (blocks * NT >= (1ll << 32)) return hipErrorInvalidConfiguration;
+    BwdArgs b = a;
+    b.xcd_major = nstream % 8 == 0 ? 1 : 0;
+    hipLaunchKernelGGL(k_bwd_dq_bf16, dim3((unsigned)blocks), dim3(NT), 0, s, b);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+}  // namespace ra

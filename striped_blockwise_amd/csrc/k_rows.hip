@@ -90,6 +90,51 @@ __global__ __launch_bounds__(256) void k_merge(float* __restrict__ o_acc, float*
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Backward row term D_i = sum_e O_ie dO_ie (fp32 sums).  16 lanes of one wavefront per row, each
+// taking groups of 4 consecutive elements (or single elements when d % 4 != 0).
+__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4(const __bf16* p) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+}
+
+template <typename TO, typename TD>
+__global__ __launch_bounds__(256) void k_delta(const TO* __restrict__ o, const TD* __restrict__ dout,
+                                               int64_t rows, int64_t d, float* __restrict__ delta) {
+  constexpr int LPR = 16;
+  const int lane = threadIdx.x & 63;
+  const int sub = lane / LPR;
+  const int li = lane % LPR;
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  const bool vec4 = (d & 3) == 0;
+  for (int64_t row0 = wave * (64 / LPR); row0 < rows; row0 += nwaves * (64 / LPR)) {
+    const int64_t row = row0 + sub;
+    float acc = 0.f;
+    if (row < rows) {
+      const TO* orow = o + row * d;
+      const TD* drow = dout + row * d;
+      if (vec4) {
+        for (int64_t j = 4 * li; j < d; j += 4 * LPR) {
+          const float4 a = load4(orow + j);
+          const float4 b = load4(drow + j);
+          acc = fmaf(a.x, b.x, acc);
+          acc = fmaf(a.y, b.y, acc);
+          acc = fmaf(a.z, b.z, acc);
+          acc = fmaf(a.w, b.w, acc);
+        }
+      } else {
+        for (int64_t j = li; j < d; j += LPR) acc = fmaf((float)orow[j], (float)drow[j], acc);
+      }
+    }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (li == 0 && row < rows) delta[row] = acc;
+  }
+}
+
 int grid_for(uint64_t work_items, int per_block) {
   uint64_t g = (work_items + per_block - 1) / per_block;
   const uint64_t cap = 256ull * 64;                       // plenty of waves for every CU
@@ -134,6 +179,20 @@ hipError_t launch_merge(float* o_acc, float* lse_acc, const float* o_part, const
     default: return hipErrorInvalidValue;
   }
 #undef RA_MERGE_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_delta(const void* o, int o_f32, const void* dout, int do_f32, int64_t rows,
+                        int64_t d, float* delta, hipStream_t s) {
+  const int grid = grid_for((uint64_t)((rows + 3) / 4) * 64, 256);
+#define RA_DELTA(TO, TD)                                                                        \
+  hipLaunchKernelGGL((k_delta<TO, TD>), dim3(grid), dim3(256), 0, s, (const TO*)o, (const TD*)dout, \
+                     rows, d, delta)
+  if (o_f32 && do_f32) RA_DELTA(float, float);
+  else if (o_f32) RA_DELTA(float, __bf16);
+  else if (do_f32) RA_DELTA(__bf16, float);
+  else RA_DELTA(__bf16, __bf16);
+#undef RA_DELTA
   return hipGetLastError();
 }
 

@@ -71,6 +71,38 @@ ra_status_t launch_attn(const ra_problem_t* pr, const ra::AttnArgs& a, hipStream
   return hip_status(e, "attention kernel launch");
 }
 
+
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  const char* x = (const char*)a;
+  const char* y = (const char*)b;
+  return x < y + bbytes && y < x + abytes;
+}
+
+ra_status_t check_bwd_support(const ra_problem_t* pr) {
+  const bool sup = pr->dtype == RA_BF16 ? ra::bwd_bf16_supported(pr->d) : ra::bwd_f32_supported(pr->d);
+  if (!sup)
+    return fail(RA_E_UNSUPPORTED, "backward: head dim %lld is not supported for %s inputs",
+                (long long)pr->d, pr->dtype == RA_BF16 ? "bf16" : "f32");
+  return ok();
+}
+
+// dq, dk, dv must be three disjoint float32 arrays of `dq_bytes` / `dkv_bytes` bytes.
+ra_status_t check_grad_outputs(const float* dq, int64_t dq_bytes, const float* dk, const float* dv,
+                               int64_t dkv_bytes) {
+  if (!aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return fail(RA_E_INVAL, "dq, dk and dv must be 16-byte aligned");
+  if (overlaps(dq, dq_bytes, dk, dkv_bytes) || overlaps(dq, dq_bytes, dv, dkv_bytes) ||
+      overlaps(dk, dkv_bytes, dv, dkv_bytes))
+    return fail(RA_E_INVAL, "dq, dk and dv must not overlap");
+  return ok();
+}
+
+ra_status_t launch_bwd(const ra_problem_t* pr, const ra::BwdArgs& a, hipStream_t s) {
+  hipError_t e = pr->dtype == RA_BF16 ? ra::launch_bwd_bf16(a, (int)pr->d, true, true, s)
+                                      : ra::launch_bwd_f32(a, (int)pr->d, true, true, s);
+  return hip_status(e, "backward kernel launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -212,6 +244,109 @@ ra_status_t ra_forward(const ra_problem_t* prob, const void* q, const void* k, c
   a.o_f32 = o_dtype == RA_F32 ? 1 : 0;
   a.stats = stats; a.stats_single = 0;
   return launch_attn(prob, a, (hipStream_t)stream);
+}
+
+ra_status_t ra_bwd_delta(const void* o, int32_t o_dtype, const void* dout, int32_t dout_dtype,
+                         int64_t rows, int64_t d, float* delta, void* stream) {
+  if (rows < 0 || d <= 0) return fail(RA_E_INVAL, "rows must be >= 0 and d > 0");
+  if ((o_dtype != RA_BF16 && o_dtype != RA_F32) || (dout_dtype != RA_BF16 && dout_dtype != RA_F32))
+    return fail(RA_E_INVAL, "o_dtype / dout_dtype must be RA_BF16 or RA_F32");
+  if (rows == 0) return ok();
+  if (!o || !dout || !delta) return fail(RA_E_INVAL, "o, dout and delta must not be NULL");
+  const size_t ao = d % 4 == 0 ? (size_t)(4 * elem_bytes(o_dtype)) : (size_t)elem_bytes(o_dtype);
+  const size_t ad = d % 4 == 0 ? (size_t)(4 * elem_bytes(dout_dtype)) : (size_t)elem_bytes(dout_dtype);
+  if (!aligned(o, ao) || !aligned(dout, ad) || !aligned(delta, 4))
+    return fail(RA_E_INVAL, "o / dout must be aligned to 4 elements when d %% 4 == 0 (else 1), delta to 4 bytes");
+  if (rows > INT64_MAX / d / 4) return fail(RA_E_INVAL, "rows*d overflows");
+  if (overlaps(delta, rows * 4, o, rows * d * elem_bytes(o_dtype)) ||
+      overlaps(delta, rows * 4, dout, rows * d * elem_bytes(dout_dtype)))
+    return fail(RA_E_INVAL, "delta must not overlap o or dout");
+  return hip_status(ra::launch_delta(o, o_dtype == RA_F32, dout, dout_dtype == RA_F32, rows, d, delta,
+                                     (hipStream_t)stream),
+                    "delta kernel launch");
+}
+
+ra_status_t ra_backward_round(const ra_problem_t* prob, const void* q, const void* k,
+                              const void* v, const void* dout, const float* lse,
+                              const float* delta, int64_t q_stride_bh, int64_t kv_stride_bh,
+                              int64_t row_stride_bh, int32_t p, int32_t kv, float* dq_acc,
+                              float* dk_acc, float* dv_acc, void* stream) {
+  ra_status_t st = ra_check(prob, p, kv);
+  if (st != RA_OK) return st;
+  st = check_bwd_support(prob);
+  if (st != RA_OK) return st;
+  if (empty_problem(prob)) return ok();
+  const int64_t c = prob->n / prob->P;
+  const int64_t d = prob->d;
+  if (!q || !k || !v || !dout || !lse || !delta || !dq_acc || !dk_acc || !dv_acc)
+    return fail(RA_E_INVAL, "q, k, v, dout, lse, delta, dq_acc, dk_acc and dv_acc must not be NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) || !aligned(lse, 4) ||
+      !aligned(delta, 4))
+    return fail(RA_E_INVAL, "q, k, v and dout must be 16-byte aligned, lse and delta 4-byte aligned");
+  const int64_t vec = 16 / elem_bytes(prob->dtype);
+  if (q_stride_bh < 0 || kv_stride_bh < 0 || row_stride_bh < 0 || q_stride_bh % vec || kv_stride_bh % vec)
+    return fail(RA_E_INVAL, "strides must be >= 0, q/kv strides multiples of %lld elements", (long long)vec);
+  const int64_t BH = prob->B * prob->H;
+  if (BH > 1 && (q_stride_bh < c * d || kv_stride_bh < c * d || row_stride_bh < c))
+    return fail(RA_E_INVAL, "strides must be at least c*d = %lld (q, kv) and c = %lld (rows) elements",
+                (long long)(c * d), (long long)c);
+  const int64_t gbytes = BH * c * d * 4;
+  st = check_grad_outputs(dq_acc, gbytes, dk_acc, dv_acc, gbytes);
+  if (st != RA_OK) return st;
+  if (ra::round_mode(prob->layout, prob->causal, p, kv) == ra::MODE_SKIP) return ok();
+  ra::BwdArgs a{};
+  a.q = q; a.dout = dout; a.lse = lse; a.delta = delta; a.k = k; a.v = v;
+  a.q_bh_stride = q_stride_bh; a.do_bh_stride = q_stride_bh;
+  a.row_bh_stride = row_stride_bh; a.kv_bh_stride = kv_stride_bh;
+  a.dq = dq_acc; a.dq_bh_stride = c * d;
+  a.dk = dk_acc; a.dv = dv_acc; a.dkv_bh_stride = c * d;
+  a.c = (int)c; a.P = prob->P; a.BH = (int)BH;
+  a.p_begin = p; a.n_dev = 1;
+  a.kv_base = kv; a.n_kv = 1;
+  a.r_begin = ra::ring_block(p, kv, prob->P); a.r_count = 1;
+  a.layout = prob->layout; a.causal = prob->causal;
+  a.scale = eff_scale(prob);
+  a.accumulate = 1;
+  return launch_bwd(prob, a, (hipStream_t)stream);
+}
+
+ra_status_t ra_backward(const ra_problem_t* prob, const void* q, const void* k, const void* v,
+                        const void* dout, const float* lse, const float* delta, int32_t p_begin,
+                        int32_t p_end, float* dq, float* dk, float* dv, void* stream) {
+  ra_status_t st = check_problem(prob);
+  if (st != RA_OK) return st;
+  st = check_bwd_support(prob);
+  if (st != RA_OK) return st;
+  if (p_begin < 0 || p_end > prob->P || p_begin >= p_end)
+    return fail(RA_E_INVAL, "device range [%d, %d) must be non-empty inside [0, %d)", p_begin, p_end, prob->P);
+  if (empty_problem(prob)) return ok();
+  if (!q || !k || !v || !dout || !lse || !delta || !dq || !dk || !dv)
+    return fail(RA_E_INVAL, "q, k, v, dout, lse, delta, dq, dk and dv must not be NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) || !aligned(lse, 4) ||
+      !aligned(delta, 4))
+    return fail(RA_E_INVAL, "q, k, v and dout must be 16-byte aligned, lse and delta 4-byte aligned");
+  const int64_t c = prob->n / prob->P;
+  const int64_t d = prob->d;
+  const int64_t BH = prob->B * prob->H;
+  const int64_t ndev = p_end - p_begin;
+  const int64_t m = ndev * c;
+  st = check_grad_outputs(dq, BH * m * d * 4, dk, dv, BH * prob->n * d * 4);
+  if (st != RA_OK) return st;
+  ra::BwdArgs a{};
+  a.q = (const char*)q + (int64_t)p_begin * c * d * elem_bytes(prob->dtype);
+  a.dout = dout; a.lse = lse; a.delta = delta; a.k = k; a.v = v;
+  a.q_bh_stride = prob->n * d; a.do_bh_stride = m * d; a.row_bh_stride = m; a.kv_bh_stride = prob->n * d;
+  a.q_dev_stride = c * d; a.do_dev_stride = c * d; a.row_dev_stride = c; a.kv_blk_stride = c * d;
+  a.dq = dq; a.dq_bh_stride = m * d;
+  a.dk = dk; a.dv = dv; a.dkv_bh_stride = prob->n * d;
+  a.c = (int)c; a.P = prob->P; a.BH = (int)BH;
+  a.p_begin = p_begin; a.n_dev = (int)ndev;
+  a.kv_base = 0; a.n_kv = prob->P;
+  a.r_begin = 0; a.r_count = prob->P;
+  a.layout = prob->layout; a.causal = prob->causal;
+  a.scale = eff_scale(prob);
+  a.accumulate = 0;
+  return launch_bwd(prob, a, (hipStream_t)stream);
 }
 
 }  // extern "C"

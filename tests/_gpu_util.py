@@ -49,3 +49,33 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, kind: str, label: str = ""):
         assert num / den <= BF16_O_RELFRO, f"{label}: O rel-Frobenius {num / den:.3e} > {BF16_O_RELFRO}"
         assert err_l <= BF16_LSE_ABS, f"{label}: LSE max-abs {err_l:.3e} > {BF16_LSE_ABS}"
     return err_o, err_l
+
+
+# Gradients (backward pass) against the fp64 oracle.  float32: same bound as the forward.
+# bf16: the kernels round P and dS to bf16 (relative error <= 2^-9 each, RMS 2^-9/sqrt(3) ~ 1.1e-3
+# for round-to-nearest) before the fp32-accumulated MFMA sums, and take O / LSE from the bf16
+# forward (LSE within 1e-3), so a gradient tensor's relative Frobenius error is ~2e-3; the
+# bounds leave 5x room.  Max-abs is taken relative to the tensor's largest reference entry.
+F32_GRAD_ABS = 1e-4
+BF16_GRAD_RELFRO = 1e-2
+BF16_GRAD_MAXREL = 2e-2
+
+
+def compare_grad(got, ref, kind: str, label: str = ""):
+    g = np64(got) if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert g.shape == ref.shape, (label, g.shape, ref.shape)
+    assert np.all(np.isfinite(g)), f"{label}: non-finite gradient"
+    err = float(np.abs(g - ref).max()) if g.size else 0.0
+    if kind == "f32":
+        assert err <= F32_GRAD_ABS, f"{label}: max-abs {err:.3e} > {F32_GRAD_ABS}"
+        return err
+    top = float(np.abs(ref).max()) if ref.size else 0.0
+    num = float(np.linalg.norm(g - ref))
+    den = float(np.linalg.norm(ref))
+    if den == 0.0:
+        assert err == 0.0, f"{label}: reference is zero, got max-abs {err:.3e}"
+        return 0.0
+    assert num / den <= BF16_GRAD_RELFRO, f"{label}: rel-Frobenius {num / den:.3e} > {BF16_GRAD_RELFRO}"
+    assert err <= BF16_GRAD_MAXREL * top, f"{label}: max-abs {err:.3e} > {BF16_GRAD_MAXREL} x {top:.3e}"
+    return num / den

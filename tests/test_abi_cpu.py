@@ -32,7 +32,8 @@ def ra():
 def test_header_declares_the_boundary():
     names = _declared()
     for want in ("ra_abi_version", "ra_last_error", "ra_check", "ra_tile_shape", "ra_permute",
-                 "ra_permute_ids", "ra_round", "ra_merge", "ra_forward"):
+                 "ra_permute_ids", "ra_round", "ra_merge", "ra_forward", "ra_bwd_delta",
+                 "ra_backward_round", "ra_backward"):
         assert want in names
 
 
@@ -44,7 +45,7 @@ def test_library_exports_every_declared_symbol(ra):
 
 
 def test_abi_version_and_tiles(ra):
-    assert ra.abi_version() == 1
+    assert ra.abi_version() == 2
     tq, tk = ra.tile_shape(ra.BF16, 128)
     assert tq > 0 and tk > 0 and tq % 32 == 0 and tk % 16 == 0
     assert ra.tile_shape(ra.F32, 64)[0] > 0
@@ -108,12 +109,36 @@ def test_raw_abi_rejects_null_and_bad_sizes_without_gpu(ra):
     assert L.ra_permute(ctypes.c_void_p(2), ctypes.c_void_p(4096), 1, 16, 8, 4, 0, None) == -1
 
 
+def test_backward_host_validation(ra):
+    """The backward entry points validate on the host and enqueue nothing on bad input."""
+    L = ra.lib()
+    N = None
+    assert L.ra_bwd_delta(N, ra.BF16, N, ra.BF16, 0, 128, N, N) == 0            # empty: no-op
+    assert L.ra_bwd_delta(N, ra.BF16, N, ra.BF16, 4, 128, N, N) == -1
+    assert L.ra_bwd_delta(N, 7, N, ra.BF16, 4, 128, N, N) == -1 and b"dtype" in L.ra_last_error()
+    assert L.ra_bwd_delta(N, ra.BF16, N, ra.BF16, 4, 0, N, N) == -1
+    pr = ra._problem(1, 1, 256, 128, 4, ra.BF16, ra.STRIPED, True, 0.0)
+    args13 = (N,) * 6
+    assert L.ra_backward(ctypes.byref(pr), *args13, 0, 4, N, N, N, N) == -1         # NULL pointers
+    assert L.ra_backward(ctypes.byref(pr), *args13, 3, 3, N, N, N, N) == -1
+    assert b"device range" in L.ra_last_error()
+    assert L.ra_backward_round(ctypes.byref(pr), *args13, 0, 0, 0, 4, 0, N, N, N, N) == -1   # p = 4
+    assert L.ra_backward_round(ctypes.byref(pr), *args13, 0, 0, 0, 1, 0, N, N, N, N) == -1   # NULL
+    bad_d = ra._problem(1, 1, 256, 64, 4, ra.BF16, ra.STRIPED, True, 0.0)
+    assert L.ra_backward(ctypes.byref(bad_d), *args13, 0, 4, N, N, N, N) == -2       # bf16 d=64
+    empty = ra._problem(1, 0, 256, 128, 4, ra.BF16, ra.STRIPED, True, 0.0)
+    assert L.ra_backward(ctypes.byref(empty), *args13, 0, 4, N, N, N, N) == 0
+    assert L.ra_backward_round(ctypes.byref(empty), *args13, 0, 0, 0, 1, 0, N, N, N, N) == 0
+
+
 def test_binding_refuses_cpu_tensors(ra):
     x = torch.zeros((1, 1, 64, 128), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         ra.forward(x, x, x, 4)
     with pytest.raises(ValueError, match="GPU"):
         ra.permute(x, 4)
+    with pytest.raises(ValueError, match="GPU"):
+        ra.backward(x, x, x, x, torch.zeros((1, 1, 64)), 4, delta=torch.zeros((1, 1, 64)))
 
 
 def test_product_package_never_touches_the_oracle():

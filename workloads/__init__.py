@@ -19,6 +19,8 @@ Recipe (every tensor is [B, H, n, d], token order, row-major, d contiguous):
   bf16 rounding; a power-of-two factor commutes with that rounding, so the stored K row equals
   8x the unscaled bf16 row.
 * Position IDs are the global token indices 0..n-1 (int64).
+* For the backward pass, the upstream gradient dO ("g") is drawn like Q, K, V with tensor_id 4,
+  as unscaled iid standard normals rounded to the compute dtype.
 
 Workload sizes follow the pages' settings: 8K, 256K and ~1M-token sequences, head dim 128, 2
 to 32 sequence-parallel devices (Striped Attention review, section 5 "experimental setup";
@@ -80,7 +82,7 @@ def get(name: str) -> Workload:
     return WORKLOADS[name]
 
 
-_TENSOR_ID = {"q": 0, "k": 1, "v": 2}
+_TENSOR_ID = {"q": 0, "k": 1, "v": 2, "g": 4}
 
 
 def _draw(seed: int, tid: int, b: int, h: int, n: int, d: int, scale: float) -> torch.Tensor:
@@ -103,7 +105,8 @@ def outlier_rows(w: Workload) -> np.ndarray:
 def qkv(w: Workload | str, which: str = "qkv", heads=None, dtype: torch.dtype | None = None):
     """Generate the workload's inputs on the CPU, in token order.
 
-    Returns a tuple of torch tensors, one per letter of ``which`` (subset of "qkv"), each
+    Returns a tuple of torch tensors, one per letter of ``which`` (letters of "qkvg"; g is the
+    upstream gradient dO of the backward pass), each
     [B, len(heads), n, d] in the workload dtype (or ``dtype`` if given: float32/float64 return
     the exactly-rounded workload-dtype values widened).  ``heads`` selects head indices (default
     all).  Deterministic for a given workload regardless of which heads are requested.
@@ -119,7 +122,7 @@ def qkv(w: Workload | str, which: str = "qkv", heads=None, dtype: torch.dtype | 
         rows = torch.from_numpy(out_rows)
         for b in range(w.B):
             for i, h in enumerate(heads):
-                x = _draw(w.seed, tid, b, h, w.n, w.d, w.input_scale)
+                x = _draw(w.seed, tid, b, h, w.n, w.d, 1.0 if letter == "g" else w.input_scale)
                 if letter == "k" and rows.numel():
                     x[rows] *= w.outlier_gain
                 t[b, i].copy_(x)                      # round-to-nearest-even to the dtype
