@@ -15,11 +15,13 @@ Also measured in the same run (reported as extra fields, never as ``value``):
   * ring: the contiguous-layout forward for device 7 (most causal work of that layout);
   * per-round ra_round times for device 7 in both layouts and their ratio;
   * the streamed path: 8 x (ra_round + ra_merge), with merge and permute GB/s;
+  * backward: ra_backward (dQ, dK, dV) of the same share in both layouts, useful TFLOP/s;
   * roofline of the dominant kernel (the fused bf16 forward) against the bf16 MFMA peak;
   * cpu_baseline: the fp64 CPU oracle on a bounded sample of the same share.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
        python bench.py --sweep      (striped/ring speedup vs sequence length; its own JSON line)
+       python bench.py --backward   (backward of the device share, both layouts; its own JSON line)
 """
 from __future__ import annotations
 
@@ -160,6 +162,46 @@ def sweep(torch, ra, dev, P: int = 8, H: int = 8, d: int = 128,
     return 0
 
 
+def backward_leg(torch, ra, w, striped_qkv, contiguous_qkv, flops_s, flops_c, p, reps=3):
+    """Backward of one device share (training), both layouts.
+
+    D = rowsum(O dO) is computed first (ra_bwd_delta), then ra_backward (the dK/dV kernel and
+    the dQ kernel) is timed with HIP events.  Useful flops: 5 matrix products of 2 d flops per
+    unmasked pair (S, dP, dV, dK, dQ), 2.5x the forward's.
+    """
+    dev = striped_qkv[0].device
+    B, H, n, d = striped_qkv[0].shape
+    P = w.P
+    c = n // P
+    gen = torch.Generator(device=dev).manual_seed(4)
+    dout = torch.randn((B, H, c, d), device=dev, generator=gen).to(torch.bfloat16)
+    o = torch.empty((B, H, c, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, c), dtype=torch.float32, device=dev)
+    dq = torch.empty((B, H, c, d), dtype=torch.float32, device=dev)
+    dk = torch.empty((B, H, n, d), dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {}
+    for layout, (qq, kk, vv), fl in (("striped", striped_qkv, flops_s), ("contiguous", contiguous_qkv, flops_c)):
+        ra.forward(qq, kk, vv, P, layout, True, p_begin=p, p_end=p + 1, out=(o, lse))
+        delta = ra.bwd_delta(o, dout)
+        ra.backward(qq, kk, vv, dout, lse, P, layout, True, p, p + 1, delta=delta, out=(dq, dk, dv))
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            ra.backward(qq, kk, vv, dout, lse, P, layout, True, p, p + 1, delta=delta, out=(dq, dk, dv))
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        tf = 2.5 * fl / (ms * 1e-3) / 1e12
+        out[layout] = {"ms": round(ms, 3), "useful_flops": 2.5 * fl, "tflops": round(tf, 3),
+                       "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+        log(f"[bench] backward {layout}: {ms:.2f} ms ({tf:.1f} TFLOP/s useful)")
+    out["share_speedup_striped_over_ring"] = round(out["contiguous"]["ms"] / out["striped"]["ms"], 4)
+    out["kernels"] = "k_bwd_dkv_bf16 then k_bwd_dq_bf16 (ra_backward); D precomputed by ra_bwd_delta"
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -168,6 +210,8 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="share_n256k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="only the timed striped steps")
+    ap.add_argument("--backward", action="store_true",
+                    help="instead of the default line: backward (dQ, dK, dV) of the device share, both layouts")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the default line: striped/ring speedup and TFLOP/s vs sequence length")
     args = ap.parse_args(argv)
@@ -211,6 +255,16 @@ def main(argv=None) -> int:
     pairs_c = useful_pairs("contiguous", P, c, p)
     flops_s = 4.0 * d * BH * sum(pairs_s)
     flops_c = 4.0 * d * BH * sum(pairs_c)
+
+    if args.backward:
+        for src, dst in ((q, qs), (k, ks), (v, vs)):
+            ra.permute(src, P, out=dst)
+        res = backward_leg(torch, ra, w, (qs, ks, vs), (q, k, v), flops_s, flops_c, p, reps=max(1, args.steps))
+        print(json.dumps({"metric": "causal blockwise-attn backward TFLOP/s (useful: 10 d flops per unmasked pair), 1 GPU",
+                          "config": {"workload": w.name, "n": w.n, "P": P, "c": c, "device": p, "B": B, "H": H,
+                                     "d": d, "causal": True, "dout": "seeded N(0,1) bf16 (GPU generator)"},
+                          "backward": res}), flush=True)
+        return 0
 
     def step():
         ra.permute(q, P, out=qs)
@@ -353,6 +407,9 @@ def main(argv=None) -> int:
         log(f"[bench] streamed {stream_ms:.2f} ms; merge {mavg:.3f} ms "
             f"({merge_bytes / (mavg * 1e-3) / 1e9:.0f} GB/s); permute {perm_ms:.3f} ms "
             f"({perm_bytes / (perm_ms * 1e-3) / 1e9:.0f} GB/s)")
+
+    if not args.no_extras:
+        result["backward"] = backward_leg(torch, ra, w, (qs, ks, vs), (q, k, v), flops_s, flops_c, p)
 
     if not args.no_extras:
         # context: a plain library GEMM (torch.matmul -> hipBLASLt), bf16, square 8192, on the

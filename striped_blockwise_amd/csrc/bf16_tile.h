@@ -91,6 +91,14 @@ __device__ __forceinline__ int a_tr_off(int lane, int db, int sec) {
   return tile_off<S>(row, 2 * d);
 }
 
+// XOR form of the same offsets, for kernels short of registers.  With any of the chunk masks,
+// the row-wise offset of step dk is a_rowwise_off(lane, 0) ^ (dk << 5) (the step index moves
+// chunk bits 1-3 only), and the transposed offset of (db, sec) is a_tr_off(lane, 0, 0) ^
+// tr_xor(db, sec) under t_swz (db moves chunk bits 2-3; sec adds 8 rows, which flips bit 3 of
+// the t_swz mask).  Tile bases that are multiples of 8 KB (and the 4 KB step between the two
+// 16-row halves of a 32-row tile) leave bits 3-11 free, so they can be added before the XOR.
+__device__ __forceinline__ constexpr int tr_xor(int db, int sec) { return (db << 6) ^ (sec ? (2048 | 128) : 0); }
+
 // Transposed A operand (rows of the tile become the contraction index): 16 tile rows starting
 // at byte offset `rows_off` within the tile, column block db.
 __device__ __forceinline__ bf16x8 read_a_tr(const char* tile, int off_lo, int off_hi) {

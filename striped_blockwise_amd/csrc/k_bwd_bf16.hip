@@ -249,7 +249,7 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dq_bf16(BwdArgs a) {
 // LDS per stage: Q tile, dO tile, then 32 floats of L and 32 of D.
 constexpr int RS_BYTES = 2 * TS * 4;
 
-__global__ __launch_bounds__(NT, 1) void k_bwd_dkv_bf16(BwdArgs a) {
+__global__ __launch_bounds__(NT, 2) void k_bwd_dkv_bf16(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE + 2 * RS_BYTES];  // Q0 Q1 O0 O1 RS0 RS1
 
   const int tid = threadIdx.x;
@@ -271,13 +271,9 @@ __global__ __launch_bounds__(NT, 1) void k_bwd_dkv_bf16(BwdArgs a) {
   const bool wave_live = kw0 < c;
   const int x = kw0 + l32;
 
-  int q_row[8], q_tr[4][2];
-#pragma unroll
-  for (int dk = 0; dk < 8; ++dk) q_row[dk] = a_rowwise_off<SWZ_T>(lane, dk);
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int sec = 0; sec < 2; ++sec) q_tr[db][sec] = a_tr_off<SWZ_T>(lane, db, sec);
+  // LDS offsets of step 0 / column block 0; the others are these XOR constants (tr_xor)
+  const int rw0 = a_rowwise_off<SWZ_T>(lane, 0);
+  const int tr0 = a_tr_off<SWZ_T>(lane, 0, 0);
   unsigned dma[DmaShape<NW, TS>::PER_WAVE];
   dma_init<NW, TS>(dma, SWZ_T, wave_u, lane);
 
@@ -335,22 +331,25 @@ __global__ __launch_bounds__(NT, 1) void k_bwd_dkv_bf16(BwdArgs a) {
     };
 
     auto compute = [&](const char* qs_, const char* os_, const char* rs_, int t, bool masked) __attribute__((always_inline)) {
-      f32x16 s = f32x16{}, dp = f32x16{};
-      {
-        bf16x8 qa[8];
+      // S = Q K^T, then P and dV^T += dO^T P before dP is formed, so that S, P and dP are never
+      // all live at once; A fragments come from LDS four at a time.
+      // LDS offsets as (lane base) ^ (constant): two registers instead of sixteen.  The empty asm
+      // makes the bases opaque so that the XORs are formed here, not hoisted out of the loop.
+      int rwb = (int)(qs_ - smem) + rw0, trb = (int)(qs_ - smem) + tr0;
+      asm volatile("" : "+v"(rwb), "+v"(trb));
+      const int dq_o = (int)(os_ - qs_);
+      auto q_rowp = [&](int dk) { return smem + (rwb ^ (dk << 5)); };
+      auto o_rowp = [&](int dk) { return smem + ((rwb + dq_o) ^ (dk << 5)); };
+      auto q_tra = [&](int ks, int db) { return read_a_tr(smem, (trb + ks * 16 * ROWB) ^ tr_xor(db, 0), (trb + ks * 16 * ROWB) ^ tr_xor(db, 1)); };
+      auto o_tra = [&](int ks, int db) { return read_a_tr(smem, (trb + dq_o + ks * 16 * ROWB) ^ tr_xor(db, 0), (trb + dq_o + ks * 16 * ROWB) ^ tr_xor(db, 1)); };
+      f32x16 s = f32x16{};
 #pragma unroll
-        for (int dk = 0; dk < 8; ++dk) qa[dk] = *reinterpret_cast<const bf16x8*>(qs_ + q_row[dk]);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int h2 = 0; h2 < 2; ++h2) {
+        bf16x8 qa[4];
 #pragma unroll
-        for (int dk = 0; dk < 8; ++dk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[dk], kf[dk], s, 0, 0, 0);
-      }
-      {
-        bf16x8 oa[8];
+        for (int j = 0; j < 4; ++j) qa[j] = *reinterpret_cast<const bf16x8*>(q_rowp(4 * h2 + j));
 #pragma unroll
-        for (int dk = 0; dk < 8; ++dk) oa[dk] = *reinterpret_cast<const bf16x8*>(os_ + q_row[dk]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int dk = 0; dk < 8; ++dk) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[dk], vf[dk], dp, 0, 0, 0);
+        for (int j = 0; j < 4; ++j) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[j], kf[4 * h2 + j], s, 0, 0, 0);
       }
       if (masked) {
         const int y0 = t * TS;
@@ -361,34 +360,49 @@ __global__ __launch_bounds__(NT, 1) void k_bwd_dkv_bf16(BwdArgs a) {
           s[rg] = vis ? s[rg] : -INFINITY;
         }
       }
-      // L and D of rows acc_row(rg, hh): four runs of 4 consecutive rows
-      float pr[16], dsv[16];
+      // P for rows acc_row(rg, hh): four runs of 4 consecutive rows of L
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const float4 l4 = *reinterpret_cast<const float4*>(rs_ + (8 * g + 4 * hh) * 4);
-        const float4 d4 = *reinterpret_cast<const float4*>(rs_ + TS * 4 + (8 * g + 4 * hh) * 4);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int rg = 4 * g + j;
-          pr[rg] = __builtin_amdgcn_exp2f(fmaf(s[rg], cs, -fmaxf(lv[j], NEG_BIG) * LOG2E));
-          dsv[rg] = pr[rg] * (dp[rg] - dv[j]);
+        for (int j = 0; j < 4; ++j)
+          s[4 * g + j] = __builtin_amdgcn_exp2f(fmaf(s[4 * g + j], cs, -fmaxf(lv[j], NEG_BIG) * LOG2E));
+      }
+      {
+        const bf16x8 p0 = pack8([&](int r) { return s[r]; }, 0);
+        const bf16x8 p1 = pack8([&](int r) { return s[r]; }, 1);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const bf16x8 o0 = o_tra(0, db);
+          const bf16x8 o1 = o_tra(1, db);
+          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o0, p0, dva[db], 0, 0, 0);
+          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o1, p1, dva[db], 0, 0, 0);
         }
       }
-      const bf16x8 p0 = pack8([&](int r) { return pr[r]; }, 0);
-      const bf16x8 p1 = pack8([&](int r) { return pr[r]; }, 1);
-      const bf16x8 s0 = pack8([&](int r) { return dsv[r]; }, 0);
-      const bf16x8 s1 = pack8([&](int r) { return dsv[r]; }, 1);
+      f32x16 dp = f32x16{};
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        bf16x8 oa[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) oa[j] = *reinterpret_cast<const bf16x8*>(o_rowp(4 * h2 + j));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[j], vf[4 * h2 + j], dp, 0, 0, 0);
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 d4 = *reinterpret_cast<const float4*>(rs_ + TS * 4 + (8 * g + 4 * hh) * 4);
+        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dp[4 * g + j] = s[4 * g + j] * (dp[4 * g + j] - dv[j]);
+      }
+      const bf16x8 s0 = pack8([&](int r) { return dp[r]; }, 0);
+      const bf16x8 s1 = pack8([&](int r) { return dp[r]; }, 1);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const bf16x8 o0 = read_a_tr(os_, q_tr[db][0], q_tr[db][1]);
-        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o0, p0, dva[db], 0, 0, 0);
-        const bf16x8 o1 = read_a_tr(os_ + 16 * ROWB, q_tr[db][0], q_tr[db][1]);
-        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o1, p1, dva[db], 0, 0, 0);
-        const bf16x8 q0 = read_a_tr(qs_, q_tr[db][0], q_tr[db][1]);
+        const bf16x8 q0 = q_tra(0, db);
+        const bf16x8 q1 = q_tra(1, db);
         dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q0, s0, dka[db], 0, 0, 0);
-        const bf16x8 q1 = read_a_tr(qs_ + 16 * ROWB, q_tr[db][0], q_tr[db][1]);
         dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q1, s1, dka[db], 0, 0, 0);
       }
     };
