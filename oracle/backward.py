@@ -30,8 +30,9 @@ __all__ = ["grads", "attention_grads", "delta", "round_grads", "ring_backward"]
 
 
 def grads(q, k, v, dout, causal: bool, pos_q=None, pos_k=None, scale=None):
-    """One head: q [m, d], k/v [N, d], dout [m, dv] -> (dq, dk, dv) as float64 numpy arrays."""
-    q, k, v, dout = (torch.tensor(np.asarray(t, dtype=np.float64)) for t in (q, k, v, dout))
+    """One head: q [m, d], k/v [N, d], dout [m, dv] (numpy or torch, any float dtype) ->
+    (dq, dk, dv) as float64 numpy arrays."""
+    q, k, v, dout = (torch.tensor(_np64(t)) for t in (q, k, v, dout))
     q.requires_grad_(True)
     k.requires_grad_(True)
     v.requires_grad_(True)

@@ -5,6 +5,8 @@
   ra_permute first, as in the timed step).  Every device of both layouts is also run once, so
   the whole sequence's striped output, un-permuted on the GPU, can be compared with the
   contiguous one.
+* The backward of device 7's share (ra_backward), both layouts: dQ on sampled rows against the
+  oracle, dK and dV through identities that hold at any size.
 * 1M-token stress (n = 1048576, P = 32, H = 8, 1% of K rows x8): device 31, striped, all 32
   rounds streamed through ra_round + ra_merge, and the same share fused with ra_forward.
 
@@ -22,7 +24,7 @@ import torch
 import workloads
 from oracle import attention as OA
 from oracle import ring as OR
-from tests._gpu_util import compare, need_gpu, np64
+from tests._gpu_util import compare, compare_grad, need_gpu, np64
 
 pytestmark = pytest.mark.gpu
 
@@ -130,6 +132,59 @@ def test_share256k_whole_sequence_equivariance(ra, share):
     o_ref, l_ref = _oracle_rows(w, heads, tokens)
     compare(_sel(o_u, heads, tokens), _sel(l_u, heads, tokens), o_ref, l_ref, "bf16", "whole-sequence striped")
     compare(_sel(o_c, heads, tokens), _sel(l_c, heads, tokens), o_ref, l_ref, "bf16", "whole-sequence contiguous")
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+def test_share256k_device7_backward(ra, share, layout):
+    """ra_backward of device 7's share at full size, as bench.py --backward runs it.
+
+    dQ is checked against the oracle on sampled query rows (a row's dQ needs only that row
+    against all keys).  dK and dV hold what device 7's queries send to all 262144 keys; the
+    oracle cannot form them at this size, so they are checked through identities that hold for
+    any input: the key gradients sum to zero over the keys (softmax ignores a shift of every key),
+    the value gradients sum to the sum of dO over the rows (each row's probabilities sum to one),
+    and sum_i q_i.dq_i = sum_j k_j.dk_j (scores are bilinear in q and k).
+    """
+    from oracle import backward as OB
+    w, q, k, v = share
+    P, c, p = w.P, w.c, w.device
+    order = OR.layout_order(w.n, P, layout)
+    (g_tok,) = workloads.qkv(w, "g")
+    if layout == "striped":
+        qs, ks, vs = (ra.permute(t, P) for t in (q, k, v))
+    else:
+        qs, ks, vs = q, k, v
+    dout = g_tok[:, :, torch.from_numpy(order[p * c:(p + 1) * c])].contiguous().cuda()
+    o, lse = ra.forward(qs, ks, vs, P, layout, True, p_begin=p, p_end=p + 1)
+    dq, dk, dv = ra.backward(qs, ks, vs, dout, lse, P, layout, True, p, p + 1, o=o)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(dq).all()) and bool(torch.isfinite(dk).all()) and bool(torch.isfinite(dv).all())
+
+    # identities, per head and head-dim column, in fp64 on the GPU
+    qd = qs[:, :, p * c:(p + 1) * c].double()
+    sum_dk = dk.double().sum(2)
+    assert float((sum_dk.abs() / dk.double().abs().sum(2)).max()) <= 1e-2, "sum_j dK_j = 0"
+    sum_dv = dv.double().sum(2)
+    sum_do = dout.double().sum(2)
+    assert float(((sum_dv - sum_do).abs() / dout.double().abs().sum(2)).max()) <= 1e-2, "sum_j dV_j = sum_i dO_i"
+    lhs = (qd * dq.double()).sum((2, 3))
+    rhs = (ks.double() * dk.double()).sum((2, 3))
+    scale = (qd * dq.double()).abs().sum((2, 3))
+    assert float(((lhs - rhs).abs() / scale).max()) <= 1e-2, "sum q.dq = sum k.dk"
+    del qd, sum_dk, sum_dv, lhs, rhs
+
+    # dQ on sampled rows against the oracle (keys in token order, positions = token index)
+    rows = _sample_rows(c, k=10)
+    heads = [0, 13, 31]
+    tokens = order[p * c + rows]
+    for i, h in enumerate(heads):
+        qh, kh, vh, gh = workloads.qkv(w, "qkvg", heads=[h])
+        t = torch.from_numpy(tokens)
+        ref, _, _ = OB.grads(qh[0, 0, t], kh[0, 0], vh[0, 0], gh[0, 0, t], True, tokens, np.arange(w.n))
+        got = _sel(dq, [h], rows)[0]
+        compare_grad(got, ref, "bf16", f"share256k {layout} dQ head {h}")
+    del qs, ks, vs, dq, dk, dv, dout, o, lse
+    torch.cuda.empty_cache()
 
 
 def test_stress1m_streamed_rounds_and_merge(ra):
