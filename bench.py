@@ -39,7 +39,8 @@ METRIC = "causal blockwise-attn TFLOP/s and % bf16 MFMA peak, ring vs striped, 1
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published
 PMC_FILE = os.path.join(ROOT, "profiles", "k_attn_bf16_share_n256k_pmc.json")
-KERNEL_SRC = os.path.join(ROOT, "striped_blockwise_amd", "csrc", "k_attn_bf16.hip")
+# the fused forward's sources: the counters in PMC_FILE are used only while these are unchanged
+KERNEL_SRCS = [os.path.join(ROOT, "striped_blockwise_amd", "csrc", f) for f in ("k_attn_bf16.hip", "bf16_tile.h")]
 
 
 def log(*a):
@@ -61,9 +62,13 @@ def useful_pairs(layout: str, P: int, c: int, p: int, causal: bool = True) -> li
     return out
 
 
-def source_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_hash(paths) -> str:
+    """sha256 of the files' bytes, concatenated in the given order."""
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def traffic_from_profile(launch_bytes_hint=None):
@@ -74,7 +79,7 @@ def traffic_from_profile(launch_bytes_hint=None):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != source_hash(KERNEL_SRC):
+    if rec.get("kernel_source_sha256") != source_hash(KERNEL_SRCS):
         return None
     return rec.get("hbm_bytes_per_launch")
 
