@@ -23,10 +23,13 @@ Modules:
                 the log-sum-exp merge, and the integer work / tile counts.
   backward   -- gradients dQ, dK, dV: autograd of the definition, and the per-(query block,
                 K/V block) chain rule a ring runs, driven by the forward's log-sum-exp.
+  rope       -- rotary position embedding applied with the striped permutation (the
+                permuted position IDs of the Striped Attention review, "位置编码处理").
 
 Pins: every function here is checked by ``tests/test_oracle_pins.py`` against closed forms,
 a library routine (torch's scaled_dot_product_attention in fp64), brute force on tiny inputs,
 and the worked partition example printed in the Striped Attention review.  The gradients are
-pinned by ``tests/test_oracle_backward_pins.py`` (finite differences, closed forms, invariants).
+pinned by ``tests/test_oracle_backward_pins.py`` (finite differences, closed forms, invariants),
+the rotary embedding by ``tests/test_oracle_rope_pins.py`` (its relative-position property).
 """
-from . import attention, backward, ring  # noqa: F401
+from . import attention, backward, ring, rope  # noqa: F401
