@@ -401,6 +401,15 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         perm_ms = a.elapsed_time(b) / 3
         perm_bytes = 2.0 * k.numel() * k.element_size()
+        # rotary embedding fused into the same permutation (one read, one write per element)
+        ra.permute_rope(q, P, "striped", out=qs)
+        a.record()
+        for _ in range(3):
+            ra.permute_rope(q, P, "striped", out=qs)
+        b.record()
+        torch.cuda.synchronize()
+        rope_ms = a.elapsed_time(b) / 3
+        ra.permute(q, P, out=qs)                       # restore the plain permuted Q
         result["streamed"] = {"rounds_plus_merges_ms": round(stream_ms, 3),
                               "tflops": round(flops_s / (stream_ms * 1e-3) / 1e12, 3)}
         result["hbm_kernels"] = {
@@ -408,10 +417,13 @@ def main(argv=None) -> int:
                       "GBps": round(merge_bytes / (mavg * 1e-3) / 1e9, 1), "peak_GBps": PEAK_HBM_GBS},
             "permute": {"ms": round(perm_ms, 4), "bytes": perm_bytes,
                         "GBps": round(perm_bytes / (perm_ms * 1e-3) / 1e9, 1), "peak_GBps": PEAK_HBM_GBS},
+            "permute_rope": {"ms": round(rope_ms, 4), "bytes": perm_bytes,
+                             "GBps": round(perm_bytes / (rope_ms * 1e-3) / 1e9, 1), "peak_GBps": PEAK_HBM_GBS},
         }
         log(f"[bench] streamed {stream_ms:.2f} ms; merge {mavg:.3f} ms "
             f"({merge_bytes / (mavg * 1e-3) / 1e9:.0f} GB/s); permute {perm_ms:.3f} ms "
-            f"({perm_bytes / (perm_ms * 1e-3) / 1e9:.0f} GB/s)")
+            f"({perm_bytes / (perm_ms * 1e-3) / 1e9:.0f} GB/s); permute+RoPE {rope_ms:.3f} ms "
+            f"({perm_bytes / (rope_ms * 1e-3) / 1e9:.0f} GB/s)")
 
     if not args.no_extras:
         result["backward"] = backward_leg(torch, ra, w, (qs, ks, vs), (q, k, v), flops_s, flops_c, p)

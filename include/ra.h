@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define RA_ABI_VERSION 2
+#define RA_ABI_VERSION 3
 
 typedef int32_t ra_status_t;
 enum {
@@ -116,6 +116,28 @@ ra_status_t ra_permute(const void* src, void* dst, int64_t BH, int64_t n, int64_
 /* ra_permute for one vector of int64 position IDs of length n. */
 ra_status_t ra_permute_ids(const int64_t* src, int64_t* dst, int64_t n, int32_t P,
                            int32_t inverse, void* stream);
+
+/* Pairings of the head dim for ra_permute_rope. */
+enum {
+  RA_ROPE_INTERLEAVED = 0,  /* pair i = elements (2i, 2i+1)   */
+  RA_ROPE_HALF = 1          /* pair i = elements (i, i + d/2) */
+};
+
+/* Rotary position embedding fused with the striped permutation (Striped Attention review,
+ * "位置编码处理": RoPE-style encodings must see the position IDs permuted like the tokens).  The
+ * pages do not define RoPE; this is RoFormer's rotary embedding: pair i of a token at position
+ * m is rotated by the angle m * base^(-2i/d), so that a rotated query-key score depends on the
+ * two positions only through their difference.
+ *   inverse == 0: dst[bh][pi(t)] = R(m_t) src[bh][t]    (token order -> rotated, layout order)
+ *   inverse != 0: dst[bh][t] = R(m_t)^T src[bh][pi(t)]  (the adjoint: carries dQ / dK back)
+ * pi is the striped permutation of ra_permute for layout RA_STRIPED and the identity for
+ * RA_CONTIGUOUS.  src, dst: BH matrices of n rows x d elements (dtype RA_BF16 or RA_F32, d even),
+ * back to back; they must not overlap.  pos: NULL (m_t = t) or device int64 [n] positions in
+ * token order.  Angles, cosines, sines and the rotation are computed in fp64 and rounded once
+ * to fp32 (and then once to bf16 for bf16 data).  Striped needs n % P == 0. */
+ra_status_t ra_permute_rope(const void* src, void* dst, const int64_t* pos, int64_t BH, int64_t n,
+                            int64_t d, int32_t dtype, int32_t P, int32_t layout, double base,
+                            int32_t style, int32_t inverse, void* stream);
 
 /* One ring round (Ring Attention review, step 2): the query block of device p against the
  * K/V block that originated on device kv, under that pair's GetMask (causal) or no mask.

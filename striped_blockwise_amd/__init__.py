@@ -17,11 +17,12 @@ import torch
 __all__ = [
     "CONTIGUOUS", "STRIPED", "BF16", "F32", "lib", "abi_version", "check", "tile_shape",
     "permute", "permute_ids", "round", "merge", "forward", "new_stats", "bwd_delta",
-    "backward_round", "backward", "RaError",
+    "backward_round", "backward", "permute_rope", "ROPE_INTERLEAVED", "ROPE_HALF", "RaError",
 ]
 
 CONTIGUOUS, STRIPED = 0, 1
 BF16, F32 = 0, 1
+ROPE_INTERLEAVED, ROPE_HALF = 0, 1
 RA_OK, RA_E_INVAL, RA_E_UNSUPPORTED, RA_E_HIP = 0, -1, -2, -3
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libra.so")
@@ -52,6 +53,8 @@ _SIGS = {
     "ra_round": (_i32, [_P, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
     "ra_merge": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _vp]),
     "ra_forward": (_i32, [_P, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _vp, _vp]),
+    "ra_permute_rope": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, ctypes.c_double, _i32,
+                               _i32, _vp]),
     "ra_bwd_delta": (_i32, [_vp, _i32, _vp, _i32, _i64, _i64, _vp, _vp]),
     "ra_backward_round": (_i32, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32,
                                  _vp, _vp, _vp, _vp]),
@@ -388,3 +391,36 @@ def backward(q, k, v, dout, lse, P: int, layout="contiguous", causal=True, p_beg
                                  int(p_begin), int(p_end), _ptr(dq), _ptr(dk), _ptr(dv), _vp(_stream(dev))),
                "ra_backward")
     return dq, dk, dv
+
+
+def permute_rope(x: torch.Tensor, P: int, layout="striped", pos=None, base: float = 10000.0,
+                 style="interleaved", inverse: bool = False, out=None) -> torch.Tensor:
+    """Rotary position embedding fused with the striped permutation of the token axis.
+
+    x: contiguous GPU tensor [..., n, d] (bfloat16 or float32, d even), token order.  Returns
+    the rows rotated by their token's position (pos: int64 [n] on the GPU, default 0..n-1) in
+    the layout order; inverse=True applies the adjoint (layout -> token order, rotated back),
+    which carries gradients dQ / dK back through it.  style: "interleaved" (pairs 2i, 2i+1) or
+    "half" (pairs i, i + d/2).
+    """
+    _gpu(x)
+    if not x.is_contiguous() or x.dim() < 2:
+        raise ValueError("x must be a contiguous [..., n, d] tensor")
+    n, d = x.shape[-2], x.shape[-1]
+    BH = x.numel() // (n * d) if n * d else 0
+    if pos is not None:
+        _gpu(x, pos)
+        if pos.dtype != torch.int64 or pos.shape != (n,) or not pos.is_contiguous():
+            raise ValueError("pos must be a contiguous int64 tensor of shape [n]")
+    if isinstance(style, str):
+        style = {"interleaved": ROPE_INTERLEAVED, "half": ROPE_HALF}[style]
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError("out must match x (shape, dtype) and be contiguous")
+    _gpu(x, out)
+    with torch.cuda.device(x.device):
+        _raise(lib().ra_permute_rope(_ptr(x), _ptr(out), _ptr(pos), BH, n, d, _dtype_code(x.dtype), int(P),
+                                     _layout(layout), float(base), int(style), 1 if inverse else 0,
+                                     _vp(_stream(x.device))), "ra_permute_rope")
+    return out

@@ -135,6 +135,54 @@ __global__ __launch_bounds__(256) void k_delta(const TO* __restrict__ o, const T
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Rotary position embedding fused with the striped permutation (Striped Attention review,
+// "位置编码处理": RoPE must see the position IDs permuted like the tokens).  Pair i of a token at
+// position m is rotated by m * base^(-2i/d) (RoFormer's rotary embedding; pairs (2i, 2i+1), or
+// (i, i + d/2) with `half`).  One wavefront per token: each lane forms the cosine and sine of
+// its pairs once, in fp64 (positions reach 10^6 and more, where an fp32 angle has lost its
+// fraction), and applies them to the token's row in every (b, h) matrix.  The rotation is also
+// done in fp64 and rounded once to fp32, then (for bf16) once more to bf16.
+//   inverse == 0: dst[bh][pi(t)] = R(m_t) src[bh][t]
+//   inverse != 0: dst[bh][t] = R(m_t)^T src[bh][pi(t)]   (the adjoint: gradients back through it)
+__device__ __forceinline__ double load_elem(const float* p) { return (double)*p; }
+__device__ __forceinline__ double load_elem(const __bf16* p) { return (double)(float)*p; }
+__device__ __forceinline__ void store_elem(float* p, double v) { *p = (float)v; }
+__device__ __forceinline__ void store_elem(__bf16* p, double v) { *p = (__bf16)(float)v; }
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_rope_permute(const T* __restrict__ src, T* __restrict__ dst,
+                                                      const int64_t* __restrict__ pos, int64_t BH,
+                                                      uint32_t n, uint32_t d, uint32_t P, uint32_t c,
+                                                      int striped, int inverse, int half, double base) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t wave = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const uint64_t nwaves = ((uint64_t)gridDim.x * blockDim.x) >> 6;
+  const uint32_t npairs = d / 2;
+  for (uint64_t tt = wave; tt < n; tt += nwaves) {
+    const uint32_t t = (uint32_t)tt;
+    const uint32_t lrow = striped ? (t % P) * c + t / P : t;
+    const uint32_t srow = inverse ? lrow : t;
+    const uint32_t drow = inverse ? t : lrow;
+    const double m = pos ? (double)pos[t] : (double)t;
+    for (uint32_t i = lane; i < npairs; i += 64) {
+      const double theta = pow(base, -2.0 * (double)i / (double)d);
+      double sn, cs;
+      sincos(m * theta, &sn, &cs);
+      if (inverse) sn = -sn;
+      const uint32_t ia = half ? i : 2 * i;
+      const uint32_t ib = half ? i + npairs : 2 * i + 1;
+      for (int64_t bh = 0; bh < BH; ++bh) {
+        const T* s = src + ((uint64_t)bh * n + srow) * d;
+        T* o = dst + ((uint64_t)bh * n + drow) * d;
+        const double xa = load_elem(s + ia), xb = load_elem(s + ib);
+        store_elem(o + ia, fma(xa, cs, -xb * sn));
+        store_elem(o + ib, fma(xa, sn, xb * cs));
+      }
+    }
+  }
+}
+
 int grid_for(uint64_t work_items, int per_block) {
   uint64_t g = (work_items + per_block - 1) / per_block;
   const uint64_t cap = 256ull * 64;                       // plenty of waves for every CU
@@ -193,6 +241,20 @@ hipError_t launch_delta(const void* o, int o_f32, const void* dout, int do_f32, 
   else if (do_f32) RA_DELTA(__bf16, float);
   else RA_DELTA(__bf16, __bf16);
 #undef RA_DELTA
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_permute(const void* src, void* dst, const int64_t* pos, int64_t BH, int64_t n, int64_t d,
+                               int f32, int P, int striped, int inverse, int half, double base,
+                               hipStream_t s) {
+  const int grid = grid_for((uint64_t)n * 64, 256);
+  const uint32_t c = (uint32_t)(n / P);
+  if (f32)
+    hipLaunchKernelGGL(k_rope_permute<float>, dim3(grid), dim3(256), 0, s, (const float*)src, (float*)dst, pos,
+                       BH, (uint32_t)n, (uint32_t)d, (uint32_t)P, c, striped, inverse, half, base);
+  else
+    hipLaunchKernelGGL(k_rope_permute<__bf16>, dim3(grid), dim3(256), 0, s, (const __bf16*)src, (__bf16*)dst,
+                       pos, BH, (uint32_t)n, (uint32_t)d, (uint32_t)P, c, striped, inverse, half, base);
   return hipGetLastError();
 }
 

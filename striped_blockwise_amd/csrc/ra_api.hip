@@ -157,6 +157,32 @@ ra_status_t ra_permute_ids(const int64_t* src, int64_t* dst, int64_t n, int32_t 
   return ra_permute(src, dst, 1, n, 8, P, inverse, stream);
 }
 
+ra_status_t ra_permute_rope(const void* src, void* dst, const int64_t* pos, int64_t BH, int64_t n,
+                            int64_t d, int32_t dtype, int32_t P, int32_t layout, double base,
+                            int32_t style, int32_t inverse, void* stream) {
+  if (BH < 0 || n < 0) return fail(RA_E_INVAL, "BH and n must be >= 0");
+  if (d <= 0 || d % 2) return fail(RA_E_INVAL, "head dim d must be positive and even (got %lld)", (long long)d);
+  if (dtype != RA_BF16 && dtype != RA_F32) return fail(RA_E_INVAL, "unknown dtype %d", dtype);
+  if (layout != RA_CONTIGUOUS && layout != RA_STRIPED) return fail(RA_E_INVAL, "unknown layout %d", layout);
+  if (style != RA_ROPE_INTERLEAVED && style != RA_ROPE_HALF) return fail(RA_E_INVAL, "unknown RoPE style %d", style);
+  if (!(base > 0.0) || !std::isfinite(base)) return fail(RA_E_INVAL, "base must be positive and finite");
+  if (P < 1) return fail(RA_E_INVAL, "P must be >= 1 (got %d)", P);
+  if (layout == RA_STRIPED && n % P != 0) return fail(RA_E_INVAL, "n (%lld) must be a multiple of P (%d)", (long long)n, P);
+  if (n > (int64_t)UINT32_MAX / 2 || d > (int64_t)UINT32_MAX / 2) return fail(RA_E_INVAL, "n or d too large");
+  if (BH == 0 || n == 0) return ok();
+  if (!src || !dst) return fail(RA_E_INVAL, "src / dst must not be NULL");
+  const int64_t eb = elem_bytes(dtype);
+  if (!aligned(src, eb) || !aligned(dst, eb) || (pos && !aligned(pos, 8)))
+    return fail(RA_E_INVAL, "src / dst must be element aligned, pos 8-byte aligned");
+  if (BH > INT64_MAX / n / d / eb) return fail(RA_E_INVAL, "BH*n*d overflows");
+  const int64_t bytes = BH * n * d * eb;
+  if (overlaps(src, bytes, dst, bytes)) return fail(RA_E_INVAL, "src and dst overlap");
+  const int Pe = layout == RA_STRIPED ? P : 1;
+  return hip_status(ra::launch_rope_permute(src, dst, pos, BH, n, d, dtype == RA_F32, Pe, layout == RA_STRIPED,
+                                            inverse ? 1 : 0, style == RA_ROPE_HALF, base, (hipStream_t)stream),
+                    "rope kernel launch");
+}
+
 ra_status_t ra_round(const ra_problem_t* prob, const void* q, const void* k, const void* v,
                      int64_t q_stride_bh, int64_t kv_stride_bh, int32_t p, int32_t kv,
                      float* o_part, float* lse_part, ra_round_stats_t* stats, void* stream) {

@@ -104,6 +104,9 @@ hipError_t launch_permute(const void* src, void* dst, int64_t BH, int64_t n, int
                           int P, int inverse, hipStream_t s);
 hipError_t launch_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
                         int64_t rows, int64_t d, hipStream_t s);
+hipError_t launch_rope_permute(const void* src, void* dst, const int64_t* pos, int64_t BH, int64_t n, int64_t d,
+                               int f32, int P, int striped, int inverse, int half, double base,
+                               hipStream_t s);
 hipError_t launch_delta(const void* o, int o_f32, const void* dout, int do_f32, int64_t rows,
                         int64_t d, float* delta, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdArgs& a, int d, bool dq, bool dkv, hipStream_t s);

@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for want in ("ra_abi_version", "ra_last_error", "ra_check", "ra_tile_shape", "ra_permute",
                  "ra_permute_ids", "ra_round", "ra_merge", "ra_forward", "ra_bwd_delta",
-                 "ra_backward_round", "ra_backward"):
+                 "ra_backward_round", "ra_backward", "ra_permute_rope"):
         assert want in names
 
 
@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(ra):
 
 
 def test_abi_version_and_tiles(ra):
-    assert ra.abi_version() == 2
+    assert ra.abi_version() == 3
     tq, tk = ra.tile_shape(ra.BF16, 128)
     assert tq > 0 and tk > 0 and tq % 32 == 0 and tk % 16 == 0
     assert ra.tile_shape(ra.F32, 64)[0] > 0
@@ -129,6 +129,22 @@ def test_backward_host_validation(ra):
     empty = ra._problem(1, 0, 256, 128, 4, ra.BF16, ra.STRIPED, True, 0.0)
     assert L.ra_backward(ctypes.byref(empty), *args13, 0, 4, N, N, N, N) == 0
     assert L.ra_backward_round(ctypes.byref(empty), *args13, 0, 0, 0, 1, 0, N, N, N, N) == 0
+
+
+def test_rope_host_validation(ra):
+    L = ra.lib()
+    N = None
+    args = lambda **kw: [kw.get(k, v) for k, v in (("src", N), ("dst", N), ("pos", N), ("BH", 1), ("n", 16),
+                                                   ("d", 8), ("dtype", ra.BF16), ("P", 4), ("layout", ra.STRIPED),
+                                                   ("base", 10000.0), ("style", ra.ROPE_INTERLEAVED),
+                                                   ("inverse", 0), ("stream", N))]
+    assert L.ra_permute_rope(*args(n=0)) == 0                       # empty: no-op
+    assert L.ra_permute_rope(*args()) == -1 and b"NULL" in L.ra_last_error()
+    assert L.ra_permute_rope(*args(d=7)) == -1 and b"even" in L.ra_last_error()
+    assert L.ra_permute_rope(*args(style=5)) == -1 and b"style" in L.ra_last_error()
+    assert L.ra_permute_rope(*args(n=18)) == -1 and b"multiple of P" in L.ra_last_error()
+    assert L.ra_permute_rope(*args(base=-1.0)) == -1
+    assert L.ra_permute_rope(*args(dtype=9)) == -1
 
 
 def test_binding_refuses_cpu_tensors(ra):
