@@ -32,7 +32,7 @@ namespace {
 using namespace bf16t;
 
 #ifndef RA_BF16_NW
-#define RA_BF16_NW 4            // wavefronts per workgroup
+#define RA_BF16_NW 12           // wavefronts per workgroup (one workgroup fills a CU at 3 waves per SIMD)
 #endif
 #ifndef RA_BF16_XMAP
 #define RA_BF16_XMAP 1          // 1: XCD-major block order (one (head, device) stream per XCD)
