@@ -35,10 +35,13 @@ namespace {
 
 using namespace bf16t;
 
-constexpr int NW = 4;            // wavefronts per workgroup
-constexpr int NT = NW * 64;
+#ifndef RA_BWD_DQ_NW
+#define RA_BWD_DQ_NW 8           // dQ kernel: wavefronts per workgroup (one workgroup per CU)
+#endif
+#ifndef RA_BWD_DKV_NW
+#define RA_BWD_DKV_NW 4          // dK/dV kernel: wavefronts per workgroup (two per CU)
+#endif
 constexpr int WR = 32;           // stationary rows per wavefront
-constexpr int WG_ROWS = NW * WR; // stationary rows per workgroup
 constexpr int TS = 32;           // streamed rows per tile
 constexpr int TILE = TS * ROWB;  // bytes of one streamed tile (8 KB)
 constexpr float NEG_BIG = -1e30f;  // clamp for L = -inf (a row that sees no key): P stays 0
@@ -97,7 +100,9 @@ __device__ __forceinline__ void store_rows(float* row, const f32x16 (&acc)[4], f
 }
 
 // ------------------------------------------------------------------------------- dQ kernel
-__global__ __launch_bounds__(NT, 2) void k_bwd_dq_bf16(BwdArgs a) {
+__global__ __launch_bounds__(RA_BWD_DQ_NW * 64, 2) void k_bwd_dq_bf16(BwdArgs a) {
+  constexpr int NW = RA_BWD_DQ_NW;
+  constexpr int WG_ROWS = NW * WR;      // stationary rows per workgroup
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];   // K0 K1 V0 V1
 
   const int tid = threadIdx.x;
@@ -249,7 +254,9 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dq_bf16(BwdArgs a) {
 // LDS per stage: Q tile, dO tile, then 32 floats of L and 32 of D.
 constexpr int RS_BYTES = 2 * TS * 4;
 
-__global__ __launch_bounds__(NT, 2) void k_bwd_dkv_bf16(BwdArgs a) {
+__global__ __launch_bounds__(RA_BWD_DKV_NW * 64, 2) void k_bwd_dkv_bf16(BwdArgs a) {
+  constexpr int NW = RA_BWD_DKV_NW;
+  constexpr int WG_ROWS = NW * WR;      // stationary rows per workgroup
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE + 2 * RS_BYTES];  // Q0 Q1 O0 O1 RS0 RS1
 
   const int tid = threadIdx.x;
@@ -437,24 +444,25 @@ bool bwd_bf16_supported(int64_t d) { return d == D; }
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, int d, bool dq, bool dkv, hipStream_t s) {
   if (d != D) return hipErrorInvalidValue;
-  const int64_t ntile = (a.c + WG_ROWS - 1) / WG_ROWS;
   if (dkv) {
+    constexpr int rows = RA_BWD_DKV_NW * WR, nt = RA_BWD_DKV_NW * 64;
     const int64_t nstream = (int64_t)a.BH * a.n_kv;
-    const int64_t blocks = ntile * nstream;
-    if (blocks * NT >= (1ll << 32)) return hipErrorInvalidConfiguration;
+    const int64_t blocks = (a.c + rows - 1) / rows * nstream;
+    if (blocks * nt >= (1ll << 32)) return hipErrorInvalidConfiguration;
     BwdArgs b = a;
     b.xcd_major = nstream % 8 == 0 ? 1 : 0;
-    hipLaunchKernelGGL(k_bwd_dkv_bf16, dim3((unsigned)blocks), dim3(NT), 0, s, b);
+    hipLaunchKernelGGL(k_bwd_dkv_bf16, dim3((unsigned)blocks), dim3(nt), 0, s, b);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (dq) {
+    constexpr int rows = RA_BWD_DQ_NW * WR, nt = RA_BWD_DQ_NW * 64;
     const int64_t nstream = (int64_t)a.BH * a.n_dev;
-    const int64_t blocks = ntile * nstream;
-    if (blocks * NT >= (1ll << 32)) return hipErrorInvalidConfiguration;
+    const int64_t blocks = (a.c + rows - 1) / rows * nstream;
+    if (blocks * nt >= (1ll << 32)) return hipErrorInvalidConfiguration;
     BwdArgs b = a;
     b.xcd_major = nstream % 8 == 0 ? 1 : 0;
-    hipLaunchKernelGGL(k_bwd_dq_bf16, dim3((unsigned)blocks), dim3(NT), 0, s, b);
+    hipLaunchKernelGGL(k_bwd_dq_bf16, dim3((unsigned)blocks), dim3(nt), 0, s, b);
     return hipGetLastError();
   }
   return hipSuccess;
