@@ -183,6 +183,84 @@ __global__ __launch_bounds__(256) void k_rope_permute(const T* __restrict__ src,
   }
 }
 
+// Vector form of k_rope_permute for head dims with 64 % (d / 8) == 0 (d = 8 .. 512, powers of
+// two): a lane owns a unit of 4 pairs -- 8 consecutive elements (interleaved pairing) or 4 + 4
+// elements d/2 apart (half pairing) -- moved with 16-byte (or 8-byte) accesses, and a wave
+// covers 64 / (d / 8) rows of the token per step.  A lane forms its 4 cosines and sines once per
+// token, as above in fp64.
+template <int N, typename T> struct Vec;
+template <> struct Vec<8, __bf16> { typedef __bf16 type __attribute__((ext_vector_type(8))); };
+template <> struct Vec<4, __bf16> { typedef __bf16 type __attribute__((ext_vector_type(4))); };
+template <> struct Vec<8, float> { typedef float type __attribute__((ext_vector_type(8))); };
+template <> struct Vec<4, float> { typedef float type __attribute__((ext_vector_type(4))); };
+
+template <int N, typename T>
+__device__ __forceinline__ void load_n(const T* p, double (&v)[N]) {
+  const typename Vec<N, T>::type x = *reinterpret_cast<const typename Vec<N, T>::type*>(p);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = (double)(float)x[i];
+}
+template <int N, typename T>
+__device__ __forceinline__ void store_n(T* p, const double (&v)[N]) {
+  typename Vec<N, T>::type x;
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = (T)(float)v[i];
+  *reinterpret_cast<typename Vec<N, T>::type*>(p) = x;
+}
+
+template <typename T, bool HALF>
+__global__ __launch_bounds__(256) void k_rope_permute_vec(const T* __restrict__ src, T* __restrict__ dst,
+                                                          const int64_t* __restrict__ pos, int64_t BH,
+                                                          uint32_t n, uint32_t d, uint32_t P, uint32_t c,
+                                                          int striped, int inverse, double base) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t wave = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const uint64_t nwaves = ((uint64_t)gridDim.x * blockDim.x) >> 6;
+  const uint32_t units = d / 8;                    // units of 4 pairs per row
+  const uint32_t rows_per_step = 64 / units;
+  const uint32_t u = lane % units;
+  const uint32_t rsub = lane / units;
+  for (uint64_t tt = wave; tt < n; tt += nwaves) {
+    const uint32_t t = (uint32_t)tt;
+    const uint32_t lrow = striped ? (t % P) * c + t / P : t;
+    const uint32_t srow = inverse ? lrow : t;
+    const uint32_t drow = inverse ? t : lrow;
+    const double m = pos ? (double)pos[t] : (double)t;
+    double cs[4], sn[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double theta = pow(base, -2.0 * (double)(4 * u + j) / (double)d);
+      sincos(m * theta, &sn[j], &cs[j]);
+      if (inverse) sn[j] = -sn[j];
+    }
+    for (int64_t bh = rsub; bh < BH; bh += rows_per_step) {
+      const T* srow_p = src + ((uint64_t)bh * n + srow) * d;
+      T* drow_p = dst + ((uint64_t)bh * n + drow) * d;
+      if (HALF) {
+        double a[4], b[4], oa[4], ob[4];
+        load_n<4>(srow_p + 4 * u, a);
+        load_n<4>(srow_p + d / 2 + 4 * u, b);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          oa[j] = fma(a[j], cs[j], -b[j] * sn[j]);
+          ob[j] = fma(a[j], sn[j], b[j] * cs[j]);
+        }
+        store_n<4>(drow_p + 4 * u, oa);
+        store_n<4>(drow_p + d / 2 + 4 * u, ob);
+      } else {
+        double e[8], o[8];
+        load_n<8>(srow_p + 8 * u, e);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          o[2 * j] = fma(e[2 * j], cs[j], -e[2 * j + 1] * sn[j]);
+          o[2 * j + 1] = fma(e[2 * j], sn[j], e[2 * j + 1] * cs[j]);
+        }
+        store_n<8>(drow_p + 8 * u, o);
+      }
+    }
+  }
+}
+
 int grid_for(uint64_t work_items, int per_block) {
   uint64_t g = (work_items + per_block - 1) / per_block;
   const uint64_t cap = 256ull * 64;                       // plenty of waves for every CU
@@ -249,12 +327,27 @@ hipError_t launch_rope_permute(const void* src, void* dst, const int64_t* pos, i
                                hipStream_t s) {
   const int grid = grid_for((uint64_t)n * 64, 256);
   const uint32_t c = (uint32_t)(n / P);
-  if (f32)
-    hipLaunchKernelGGL(k_rope_permute<float>, dim3(grid), dim3(256), 0, s, (const float*)src, (float*)dst, pos,
-                       BH, (uint32_t)n, (uint32_t)d, (uint32_t)P, c, striped, inverse, half, base);
-  else
-    hipLaunchKernelGGL(k_rope_permute<__bf16>, dim3(grid), dim3(256), 0, s, (const __bf16*)src, (__bf16*)dst,
-                       pos, BH, (uint32_t)n, (uint32_t)d, (uint32_t)P, c, striped, inverse, half, base);
+  // vector path: rows of d % 8 == 0 elements from 32-byte aligned bases keep every lane's 8-element
+  // (or 4-element) access aligned to its own size
+  const bool vec = d % 8 == 0 && d / 8 <= 64 && 64 % (d / 8) == 0 &&
+                   (uintptr_t)src % 32 == 0 && (uintptr_t)dst % 32 == 0;
+#define RA_ROPE(K, T, ...)                                                                       \
+  hipLaunchKernelGGL(K, dim3(grid), dim3(256), 0, s, (const T*)src, (T*)dst, pos, BH, (uint32_t)n, \
+                     (uint32_t)d, (uint32_t)P, c, striped, inverse, __VA_ARGS__)
+  if (vec) {
+    if (f32) {
+      if (half) RA_ROPE((k_rope_permute_vec<float, true>), float, base);
+      else RA_ROPE((k_rope_permute_vec<float, false>), float, base);
+    } else {
+      if (half) RA_ROPE((k_rope_permute_vec<__bf16, true>), __bf16, base);
+      else RA_ROPE((k_rope_permute_vec<__bf16, false>), __bf16, base);
+    }
+  } else if (f32) {
+    RA_ROPE(k_rope_permute<float>, float, half, base);
+  } else {
+    RA_ROPE(k_rope_permute<__bf16>, __bf16, half, base);
+  }
+#undef RA_ROPE
   return hipGetLastError();
 }
 
