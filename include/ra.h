@@ -195,7 +195,8 @@ ra_status_t ra_bwd_delta(const void* o, int32_t o_dtype, const void* dout, int32
                          int64_t rows, int64_t d, float* delta, void* stream);
 
 /* Backward of one ring round: the query block of device p against the K/V block kv.
- *   q, dout: device p's rows, B*H matrices of c x d, q_stride_bh elements apart
+ *   q:       device p's rows, B*H matrices of c x d, q_stride_bh elements apart
+ *   dout:    the same rows' dO, B*H matrices of c x d, do_stride_bh elements apart
  *   k, v:    block kv, B*H matrices of c x d, kv_stride_bh elements apart
  *   lse, delta: device p's rows, B*H vectors of c float32, row_stride_bh elements apart;
  *            lse is the FINAL log-sum-exp of the rows over all keys (ra_forward's, or the
@@ -205,9 +206,9 @@ ra_status_t ra_bwd_delta(const void* o, int32_t o_dtype, const void* dout, int32
  * A pair with no visible key (contiguous block from a later device) adds nothing. */
 ra_status_t ra_backward_round(const ra_problem_t* prob, const void* q, const void* k,
                               const void* v, const void* dout, const float* lse,
-                              const float* delta, int64_t q_stride_bh, int64_t kv_stride_bh,
-                              int64_t row_stride_bh, int32_t p, int32_t kv, float* dq_acc,
-                              float* dk_acc, float* dv_acc, void* stream);
+                              const float* delta, int64_t q_stride_bh, int64_t do_stride_bh,
+                              int64_t kv_stride_bh, int64_t row_stride_bh, int32_t p, int32_t kv,
+                              float* dq_acc, float* dk_acc, float* dv_acc, void* stream);
 
 /* All rounds of the devices p_begin <= p < p_end, fused (the backward of ra_forward).
  *   q, k, v: full [B, H, n, d] tensors in layout order (contiguous)

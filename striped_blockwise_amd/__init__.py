@@ -56,7 +56,7 @@ _SIGS = {
     "ra_permute_rope": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, ctypes.c_double, _i32,
                                _i32, _vp]),
     "ra_bwd_delta": (_i32, [_vp, _i32, _vp, _i32, _i64, _i64, _vp, _vp]),
-    "ra_backward_round": (_i32, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32,
+    "ra_backward_round": (_i32, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _i32,
                                  _vp, _vp, _vp, _vp]),
     "ra_backward": (_i32, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp]),
 }
@@ -315,8 +315,8 @@ def backward_round(q_blk, k_blk, v_blk, dout_blk, lse_blk, delta_blk, P: int, p:
                    layout="contiguous", causal=True, scale: float = 0.0, grads=None):
     """Backward of one ring round: device p's query block against K/V block kv.
 
-    q_blk, dout_blk: [B, H, c, d] views with one (b, h) stride; k_blk, v_blk: [B, H, c, d]
-    views; lse_blk, delta_blk: float32 [B, H, c] views (lse: the rows' final log-sum-exp).
+    q_blk, dout_blk, k_blk, v_blk: [B, H, c, d] views (rows contiguous; k and v with one (b, h)
+    stride); lse_blk, delta_blk: float32 [B, H, c] views (lse: the rows' final log-sum-exp).
     grads: None or (dq_acc, dk_acc, dv_acc), contiguous float32 [B, H, c, d] accumulators that
     the pair's contributions are added to (new zeroed ones when None).  Returns the three.
     """
@@ -326,8 +326,7 @@ def backward_round(q_blk, k_blk, v_blk, dout_blk, lse_blk, delta_blk, P: int, p:
         if t.shape != q_blk.shape or t.dtype != q_blk.dtype:
             raise ValueError("q, k, v and dout blocks must share a shape and dtype")
     sq = _block_strides(q_blk, "q")
-    if _block_strides(dout_blk, "dout") != sq:
-        raise ValueError("q and dout must have the same (b, h) stride")
+    sdo = _block_strides(dout_blk, "dout")
     sk = _block_strides(k_blk, "k")
     if _block_strides(v_blk, "v") != sk:
         raise ValueError("k and v must have the same (b, h) stride")
@@ -343,7 +342,7 @@ def backward_round(q_blk, k_blk, v_blk, dout_blk, lse_blk, delta_blk, P: int, p:
     pr = _problem(B, H, c * P, d, P, _dtype_code(q_blk.dtype), layout, causal, scale)
     with torch.cuda.device(dev):
         _raise(lib().ra_backward_round(ctypes.byref(pr), _ptr(q_blk), _ptr(k_blk), _ptr(v_blk), _ptr(dout_blk),
-                                       _ptr(lse_blk), _ptr(delta_blk), sq, sk, sr, int(p), int(kv),
+                                       _ptr(lse_blk), _ptr(delta_blk), sq, sdo, sk, sr, int(p), int(kv),
                                        _ptr(grads[0]), _ptr(grads[1]), _ptr(grads[2]), _vp(_stream(dev))),
                "ra_backward_round")
     return grads

@@ -294,9 +294,9 @@ ra_status_t ra_bwd_delta(const void* o, int32_t o_dtype, const void* dout, int32
 
 ra_status_t ra_backward_round(const ra_problem_t* prob, const void* q, const void* k,
                               const void* v, const void* dout, const float* lse,
-                              const float* delta, int64_t q_stride_bh, int64_t kv_stride_bh,
-                              int64_t row_stride_bh, int32_t p, int32_t kv, float* dq_acc,
-                              float* dk_acc, float* dv_acc, void* stream) {
+                              const float* delta, int64_t q_stride_bh, int64_t do_stride_bh,
+                              int64_t kv_stride_bh, int64_t row_stride_bh, int32_t p, int32_t kv,
+                              float* dq_acc, float* dk_acc, float* dv_acc, void* stream) {
   ra_status_t st = ra_check(prob, p, kv);
   if (st != RA_OK) return st;
   st = check_bwd_support(prob);
@@ -310,11 +310,12 @@ ra_status_t ra_backward_round(const ra_problem_t* prob, const void* q, const voi
       !aligned(delta, 4))
     return fail(RA_E_INVAL, "q, k, v and dout must be 16-byte aligned, lse and delta 4-byte aligned");
   const int64_t vec = 16 / elem_bytes(prob->dtype);
-  if (q_stride_bh < 0 || kv_stride_bh < 0 || row_stride_bh < 0 || q_stride_bh % vec || kv_stride_bh % vec)
-    return fail(RA_E_INVAL, "strides must be >= 0, q/kv strides multiples of %lld elements", (long long)vec);
+  if (q_stride_bh < 0 || do_stride_bh < 0 || kv_stride_bh < 0 || row_stride_bh < 0 || q_stride_bh % vec ||
+      do_stride_bh % vec || kv_stride_bh % vec)
+    return fail(RA_E_INVAL, "strides must be >= 0, q/dout/kv strides multiples of %lld elements", (long long)vec);
   const int64_t BH = prob->B * prob->H;
-  if (BH > 1 && (q_stride_bh < c * d || kv_stride_bh < c * d || row_stride_bh < c))
-    return fail(RA_E_INVAL, "strides must be at least c*d = %lld (q, kv) and c = %lld (rows) elements",
+  if (BH > 1 && (q_stride_bh < c * d || do_stride_bh < c * d || kv_stride_bh < c * d || row_stride_bh < c))
+    return fail(RA_E_INVAL, "strides must be at least c*d = %lld (q, dout, kv) and c = %lld (rows) elements",
                 (long long)(c * d), (long long)c);
   const int64_t gbytes = BH * c * d * 4;
   st = check_grad_outputs(dq_acc, gbytes, dk_acc, dv_acc, gbytes);
@@ -322,7 +323,7 @@ ra_status_t ra_backward_round(const ra_problem_t* prob, const void* q, const voi
   if (ra::round_mode(prob->layout, prob->causal, p, kv) == ra::MODE_SKIP) return ok();
   ra::BwdArgs a{};
   a.q = q; a.dout = dout; a.lse = lse; a.delta = delta; a.k = k; a.v = v;
-  a.q_bh_stride = q_stride_bh; a.do_bh_stride = q_stride_bh;
+  a.q_bh_stride = q_stride_bh; a.do_bh_stride = do_stride_bh;
   a.row_bh_stride = row_stride_bh; a.kv_bh_stride = kv_stride_bh;
   a.dq = dq_acc; a.dq_bh_stride = c * d;
   a.dk = dk_acc; a.dv = dv_acc; a.dkv_bh_stride = c * d;

@@ -122,13 +122,13 @@ def test_backward_host_validation(ra):
     assert L.ra_backward(ctypes.byref(pr), *args13, 0, 4, N, N, N, N) == -1         # NULL pointers
     assert L.ra_backward(ctypes.byref(pr), *args13, 3, 3, N, N, N, N) == -1
     assert b"device range" in L.ra_last_error()
-    assert L.ra_backward_round(ctypes.byref(pr), *args13, 0, 0, 0, 4, 0, N, N, N, N) == -1   # p = 4
-    assert L.ra_backward_round(ctypes.byref(pr), *args13, 0, 0, 0, 1, 0, N, N, N, N) == -1   # NULL
+    assert L.ra_backward_round(ctypes.byref(pr), *args13, 0, 0, 0, 0, 4, 0, N, N, N, N) == -1   # p = 4
+    assert L.ra_backward_round(ctypes.byref(pr), *args13, 0, 0, 0, 0, 1, 0, N, N, N, N) == -1   # NULL
     bad_d = ra._problem(1, 1, 256, 64, 4, ra.BF16, ra.STRIPED, True, 0.0)
     assert L.ra_backward(ctypes.byref(bad_d), *args13, 0, 4, N, N, N, N) == -2       # bf16 d=64
     empty = ra._problem(1, 0, 256, 128, 4, ra.BF16, ra.STRIPED, True, 0.0)
     assert L.ra_backward(ctypes.byref(empty), *args13, 0, 4, N, N, N, N) == 0
-    assert L.ra_backward_round(ctypes.byref(empty), *args13, 0, 0, 0, 1, 0, N, N, N, N) == 0
+    assert L.ra_backward_round(ctypes.byref(empty), *args13, 0, 0, 0, 0, 1, 0, N, N, N, N) == 0
 
 
 def test_rope_host_validation(ra):

@@ -6,7 +6,9 @@
   the whole sequence's striped output, un-permuted on the GPU, can be compared with the
   contiguous one.
 * The backward of device 7's share (ra_backward), both layouts: dQ on sampled rows against the
-  oracle, dK and dV through identities that hold at any size.
+  oracle, dK and dV through identities that hold at any size; the same share streamed round by
+  round through ra_backward_round equals the fused result; and the backward of the 1M stress
+  share (device 31) under the same checks.
 * 1M-token stress (n = 1048576, P = 32, H = 8, 1% of K rows x8): device 31, striped, all 32
   rounds streamed through ra_round + ra_merge, and the same share fused with ra_forward.
 
@@ -184,6 +186,74 @@ def test_share256k_device7_backward(ra, share, layout):
         got = _sel(dq, [h], rows)[0]
         compare_grad(got, ref, "bf16", f"share256k {layout} dQ head {h}")
     del qs, ks, vs, dq, dk, dv, dout, o, lse
+    torch.cuda.empty_cache()
+
+
+def test_share256k_backward_rounds_equal_fused(ra, share):
+    """ra_backward_round over device 7's 8 rounds (dQ accumulated in place, dK/dV per block, as
+    the travelling ring buffers would hold them) against the fused ra_backward, striped."""
+    w, q, k, v = share
+    P, c, p = w.P, w.c, w.device
+    qs, ks, vs = (ra.permute(t, P) for t in (q, k, v))
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    dout = torch.randn((w.B, w.H, c, w.d), device="cuda", generator=gen).to(torch.bfloat16)
+    o, lse = ra.forward(qs, ks, vs, P, "striped", True, p_begin=p, p_end=p + 1)
+    delta = ra.bwd_delta(o, dout)
+    dq, dk, dv = ra.backward(qs, ks, vs, dout, lse, P, "striped", True, p, p + 1, delta=delta)
+    dq_r = torch.zeros_like(dq)
+    rows = slice(p * c, (p + 1) * c)
+    worst = 0.0
+    for r in range(P):
+        kb = OR.kv_block(p, r, P)
+        keys = slice(kb * c, (kb + 1) * c)
+        acc = (dq_r, torch.zeros_like(dk[:, :, keys]), torch.zeros_like(dv[:, :, keys]))
+        ra.backward_round(qs[:, :, rows], ks[:, :, keys], vs[:, :, keys], dout, lse, delta, P, p, kb,
+                          "striped", True, grads=acc)
+        for name, a_, b_ in (("dk", acc[1], dk[:, :, keys]), ("dv", acc[2], dv[:, :, keys])):
+            diff = float((a_ - b_).abs().max())
+            worst = max(worst, diff / max(1e-30, float(b_.abs().max())))
+            assert diff <= 1e-5 * float(b_.abs().max()), (name, kb, diff)
+        del acc
+    torch.cuda.synchronize()
+    diff = float((dq_r - dq).abs().max())
+    assert diff <= 1e-5 * float(dq.abs().max()), diff
+    print(f"[fullsize] streamed backward vs fused: worst relative max diff {worst:.2e}", flush=True)
+    del qs, ks, vs, dq, dk, dv, dq_r, dout, o, lse, delta
+    torch.cuda.empty_cache()
+
+
+def test_stress1m_backward(ra):
+    """Backward of device 31's share of the 1M-token stress sequence (1% of K rows x8): dQ on
+    sampled rows against the oracle, dK/dV through the key-shift, row-sum and bilinearity
+    identities (see test_share256k_device7_backward)."""
+    from oracle import backward as OB
+    w = workloads.get("stress_n1m")
+    P, c, p = w.P, w.c, w.device
+    print(f"[fullsize] generating {w.name} with dO", flush=True)
+    q, k, v, g = workloads.qkv(w, "qkvg")
+    order = OR.layout_order(w.n, P, "striped")
+    qs, ks, vs = (ra.permute(t.cuda(), P) for t in (q, k, v))
+    dout = g[:, :, torch.from_numpy(order[p * c:(p + 1) * c])].contiguous().cuda()
+    del g
+    o, lse = ra.forward(qs, ks, vs, P, "striped", True, p_begin=p, p_end=p + 1)
+    dq, dk, dv = ra.backward(qs, ks, vs, dout, lse, P, "striped", True, p, p + 1, o=o)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(dq).all()) and bool(torch.isfinite(dk).all()) and bool(torch.isfinite(dv).all())
+    qd = qs[:, :, p * c:(p + 1) * c].double()
+    assert float((dk.double().sum(2).abs() / dk.double().abs().sum(2)).max()) <= 1e-2
+    assert float(((dv.double().sum(2) - dout.double().sum(2)).abs() / dout.double().abs().sum(2)).max()) <= 1e-2
+    lhs = (qd * dq.double()).sum((2, 3))
+    rhs = (ks.double() * dk.double()).sum((2, 3))
+    assert float(((lhs - rhs).abs() / (qd * dq.double()).abs().sum((2, 3))).max()) <= 1e-2
+    del qd, dk, dv, qs, ks, vs
+    rows = _sample_rows(c, k=10)
+    tokens = order[p * c + rows]
+    t = torch.from_numpy(tokens)
+    for h in (0, 5):
+        ref, _, _ = OB.grads(q[0, h, t], k[0, h], v[0, h], dout[0, h, torch.from_numpy(rows).cuda()].cpu(),
+                             True, tokens, np.arange(w.n))
+        compare_grad(_sel(dq, [h], rows)[0], ref, "bf16", f"stress1m dQ head {h}")
+    del dq, dout, o, lse
     torch.cuda.empty_cache()
 
 
