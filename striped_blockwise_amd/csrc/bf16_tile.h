@@ -99,8 +99,9 @@ __device__ __forceinline__ int a_tr_off(int lane, int db, int sec) {
 // 16-row halves of a 32-row tile) leave bits 3-11 free, so they can be added before the XOR.
 __device__ __forceinline__ constexpr int tr_xor(int db, int sec) { return (db << 6) ^ (sec ? (2048 | 128) : 0); }
 
-// Transposed A operand (rows of the tile become the contraction index): 16 tile rows starting
-// at byte offset `rows_off` within the tile, column block db.
+// Transposed A operand (rows of the tile become the contraction index): the two 8-byte
+// ds_read_b64_tr_b16 reads at `tile` + a_tr_off(lane, db, 0) / a_tr_off(lane, db, 1) give the
+// lane's column 32 db + lane % 32 over the 16 rows of one contraction step.
 __device__ __forceinline__ bf16x8 read_a_tr(const char* tile, int off_lo, int off_hi) {
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off_lo));
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off_hi));
