@@ -5,15 +5,18 @@ Workload (default ``share_n256k``): one device's share of a 262144-token sequenc
 P = 8 (virtual) devices -- the query block of device 7 (c = 32768 tokens) against all 8 K/V
 blocks, B = 1, H = 32, d = 128, bf16, causal.
 
-One timed step = the striped hot path over that share:
-  ra_permute of Q, K, V (full sequence) and of the position IDs into the striped layout,
-  then ra_forward for device 7 (all 8 ring rounds fused, GetMask per round, tile skipping).
+One timed step = the striped hot path over that share: ra_forward for device 7 on the
+token-order Q, K, V with layout RA_STRIPED_TOKENS (all 8 ring rounds fused, GetMask per round,
+tile skipping; the striped permutation applied in the kernel's addressing: row y of block k is
+token y*P + k, and O / LSE are written back to token rows y*P + 7).
 ``value`` is useful causal TFLOP/s of the step: 4 * d * (unmasked query-key pairs) * B * H
 flops divided by the step time (masked halves of diagonal tiles and softmax work excluded).
 
 Also measured in the same run (reported as extra fields, never as ``value``):
   * ring: the contiguous-layout forward for device 7 (most causal work of that layout);
   * per-round ra_round times for device 7 in both layouts and their ratio;
+  * the same share through an explicit permutation pass: ra_permute of Q, K, V and of the
+    position IDs, then ra_forward on the permuted tensors (RA_STRIPED);
   * the streamed path: 8 x (ra_round + ra_merge), with merge and permute GB/s;
   * backward: ra_backward (dQ, dK, dV) of the same share in both layouts, useful TFLOP/s;
   * roofline of the dominant kernel (the fused bf16 forward) against the bf16 MFMA peak;
@@ -255,6 +258,8 @@ def main(argv=None) -> int:
     ids_s = torch.empty_like(ids)
     o = torch.empty((B, H, c, d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, H, c), dtype=torch.float32, device=dev)
+    o_t = torch.empty((B, H, w.n, d), dtype=torch.bfloat16, device=dev)     # token order: rows t = p mod P written
+    lse_t = torch.empty((B, H, w.n), dtype=torch.float32, device=dev)
 
     pairs_s = useful_pairs("striped", P, c, p)
     pairs_c = useful_pairs("contiguous", P, c, p)
@@ -272,13 +277,20 @@ def main(argv=None) -> int:
         return 0
 
     def step():
+        e_f0.record()
+        ra.forward(q, k, v, P, "striped_tokens", True, p_begin=p, p_end=p + 1, out=(o_t, lse_t))
+        e_f1.record()
+
+    def permuted_step(ev_fwd=None):
         ra.permute(q, P, out=qs)
         ra.permute(k, P, out=ks)
         ra.permute(v, P, out=vs)
         ra.permute_ids(ids, P, out=ids_s)
-        e_f0.record()
+        if ev_fwd:
+            ev_fwd[0].record()
         ra.forward(qs, ks, vs, P, "striped", True, p_begin=p, p_end=p + 1, out=(o, lse))
-        e_f1.record()
+        if ev_fwd:
+            ev_fwd[1].record()
 
     e_f0, e_f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for _ in range(args.warmup):
@@ -311,8 +323,8 @@ def main(argv=None) -> int:
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1)*0.5 bf16 Q/K/V, generated on the host)",
         "config": {"workload": w.name, "n": w.n, "P": P, "c": c, "device": p, "B": B, "H": H, "d": d,
-                   "layout": "striped", "causal": True,
-                   "step": "ra_permute Q,K,V,pos -> ra_forward(device p, all P rounds)",
+                   "layout": "striped_tokens", "causal": True,
+                   "step": "ra_forward(device p, all P rounds, RA_STRIPED_TOKENS: permutation in the addressing)",
                    "useful_flops_per_step": flops_s},
         "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 3),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
@@ -322,9 +334,27 @@ def main(argv=None) -> int:
         "wall_s_timed": round(wall, 3),
     }
 
+    permuted_step()                                    # qs, ks, vs: the permuted inputs for the extras
+    torch.cuda.synchronize()
     if not args.no_extras:
-        # ---- ring (contiguous) forward for the same device
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # ---- the same share through an explicit permutation pass (RA_STRIPED)
+        reps = max(3, args.steps // 2)
+        pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        a.record()
+        for i in range(reps):
+            permuted_step(pev[i])
+        b.record()
+        torch.cuda.synchronize()
+        pstep_ms = a.elapsed_time(b) / reps
+        pfwd_ms = sum(x.elapsed_time(y) for x, y in pev) / reps
+        result["permuted_step"] = {"step": "ra_permute Q,K,V,pos -> ra_forward(RA_STRIPED)",
+                                   "ms": round(pstep_ms, 4),
+                                   "tflops": round(flops_s / (pstep_ms * 1e-3) / 1e12, 3),
+                                   "forward_ms": round(pfwd_ms, 4)}
+        log(f"[bench] permute + forward step {pstep_ms:.2f} ms ({flops_s / (pstep_ms * 1e-3) / 1e12:.1f} TFLOP/s)")
+
+        # ---- ring (contiguous) forward for the same device
         reps = max(3, args.steps // 2)
         ra.forward(q, k, v, P, "contiguous", True, p_begin=p, p_end=p + 1, out=(o, lse))
         torch.cuda.synchronize()

@@ -22,9 +22,11 @@
  *
  * Conventions shared by every entry point
  *   - Tensors are row-major.  Q, K, V, O are [B, H, n, d] (or [B, H, c, d] for one block),
- *     d contiguous, the token axis in layout order (contiguous or striped).  LSE is [B, H, n]
- *     (or [B, H, c]) float32, natural-log log-sum-exp of the scaled, masked scores of the row.
- *   - Device p's block is the token rows [p*c, (p+1)*c) of the layout-ordered tensor.
+ *     d contiguous, the token axis in layout order (contiguous or striped; token order for
+ *     RA_STRIPED_TOKENS).  LSE is [B, H, n] (or [B, H, c]) float32, natural-log log-sum-exp of
+ *     the scaled, masked scores of the row.
+ *   - Device p's block is the token rows [p*c, (p+1)*c) of the layout-ordered tensor (rows
+ *     p, p+P, ... of the token-order tensor for RA_STRIPED_TOKENS).
  *   - Every pointer argument is DEVICE memory owned by the caller unless stated otherwise; the
  *     library keeps no allocation between calls and never frees caller memory.
  *   - Calls only enqueue work on `stream` (a hipStream_t; NULL = the default stream) and never
@@ -44,13 +46,13 @@
 extern "C" {
 #endif
 
-#define RA_ABI_VERSION 3
+#define RA_ABI_VERSION 4
 
 typedef int32_t ra_status_t;
 enum {
   RA_OK = 0,
   RA_E_INVAL = -1,        /* bad argument: null/misaligned pointer, index out of range, n % P != 0 */
-  RA_E_UNSUPPORTED = -2,  /* valid but not implemented: head dim or dtype combination */
+  RA_E_UNSUPPORTED = -2,  /* valid but not implemented: head dim, dtype or layout combination */
   RA_E_HIP = -3           /* the HIP runtime reported an error when launching */
 };
 
@@ -59,8 +61,13 @@ enum { RA_BF16 = 0, RA_F32 = 1 };
 
 /* Token layout of the Q/K/V rows. */
 enum {
-  RA_CONTIGUOUS = 0,  /* device p owns tokens [p*c, (p+1)*c)                                   */
-  RA_STRIPED = 1      /* device p owns tokens p, p+P, p+2P, ... (rows already permuted, ra_permute) */
+  RA_CONTIGUOUS = 0,      /* device p owns tokens [p*c, (p+1)*c)                                  */
+  RA_STRIPED = 1,         /* device p owns tokens p, p+P, p+2P, ... (rows already permuted,
+                             ra_permute)                                                          */
+  RA_STRIPED_TOKENS = 2   /* the partition and masks of RA_STRIPED, with the tensors left in token
+                             order: row y of device p's block is token row y*P + p, and the
+                             kernels apply the permutation in their addressing.  ra_forward and
+                             ra_permute_rope (identity permutation) only; P <= 65536.            */
 };
 
 /* One attention problem.  Plain host struct, passed by pointer. */
@@ -168,6 +175,10 @@ ra_status_t ra_merge(float* o_acc, float* lse_acc, const float* o_part, const fl
  *   q, k, v: full [B, H, n, d] tensors in layout order (contiguous)
  *   o:   [B, H, (p_end - p_begin) * c, d] in o_dtype (RA_BF16 or RA_F32), rows of device
  *        p_begin first; lse: NULL or [B, H, (p_end - p_begin) * c] float32
+ *   RA_STRIPED_TOKENS: q, k, v, o and lse are all in token order, o [B, H, n, d] and lse
+ *        [B, H, n]; only the rows of the selected devices (tokens t with p_begin <= t mod P
+ *        < p_end) are written, so the range 0..P gives causal attention over the sequence with
+ *        no permutation pass before or after
  *   stats: NULL or device memory [P][P] ra_round_stats_t indexed [p][r]; counts are added
  *          (zero it first); only rows p_begin..p_end-1 are touched. */
 ra_status_t ra_forward(const ra_problem_t* prob, const void* q, const void* k, const void* v,

@@ -5,7 +5,10 @@ C ABI (include/ra.h); PyTorch provides device memory and the current stream.  Th
 fallback: if libra.so is missing or the tensors are not on a GPU the calls raise.
 
 Layout names: "contiguous" (device p owns tokens [p*c, (p+1)*c); Ring Attention review, step 1)
-and "striped" (device p owns tokens p, p+P, ...; Striped Attention review, "分区策略对比").
+and "striped" (device p owns tokens p, p+P, ...; Striped Attention review, "分区策略对比"), with
+the rows permuted into layout order by ``permute``; "striped_tokens" is the striped partition
+with the tensors left in token order (``forward`` and ``permute_rope`` only): the kernels read
+and write row y of device p's block at token y*P + p.
 """
 from __future__ import annotations
 
@@ -15,12 +18,12 @@ import os
 import torch
 
 __all__ = [
-    "CONTIGUOUS", "STRIPED", "BF16", "F32", "lib", "abi_version", "check", "tile_shape",
+    "CONTIGUOUS", "STRIPED", "STRIPED_TOKENS", "BF16", "F32", "lib", "abi_version", "check", "tile_shape",
     "permute", "permute_ids", "round", "merge", "forward", "new_stats", "bwd_delta",
     "backward_round", "backward", "permute_rope", "ROPE_INTERLEAVED", "ROPE_HALF", "RaError",
 ]
 
-CONTIGUOUS, STRIPED = 0, 1
+CONTIGUOUS, STRIPED, STRIPED_TOKENS = 0, 1, 2
 BF16, F32 = 0, 1
 ROPE_INTERLEAVED, ROPE_HALF = 0, 1
 RA_OK, RA_E_INVAL, RA_E_UNSUPPORTED, RA_E_HIP = 0, -1, -2, -3
@@ -89,7 +92,8 @@ def _raise(status: int, what: str):
 
 def _layout(x) -> int:
     if isinstance(x, str):
-        return {"contiguous": CONTIGUOUS, "ring": CONTIGUOUS, "striped": STRIPED}[x]
+        return {"contiguous": CONTIGUOUS, "ring": CONTIGUOUS, "striped": STRIPED,
+                "striped_tokens": STRIPED_TOKENS}[x]
     return int(x)
 
 
@@ -252,6 +256,9 @@ def forward(q, k, v, P: int, layout="contiguous", causal=True, p_begin: int = 0,
     q, k, v: contiguous [B, H, n, d] in layout order.  Returns (o, lse): o is
     [B, H, (p_end-p_begin)*c, d] in o_dtype (default: q's dtype), lse the matching float32
     log-sum-exp (None if want_lse is False).  stats: None or new_stats(P).
+    layout "striped_tokens": q, k, v, o and lse in token order, o [B, H, n, d] and lse [B, H, n];
+    rows of devices outside the range are left as they were (zeros when out is None).
+    out: None or (o, lse) of those shapes, contiguous (lse may be None).
     """
     dev = _gpu(q, k, v)
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
@@ -263,13 +270,20 @@ def forward(q, k, v, P: int, layout="contiguous", causal=True, p_begin: int = 0,
     B, H, n, d = q.shape
     p_end = P if p_end is None else p_end
     c = n // P if P > 0 else 0
-    rows = max(0, p_end - p_begin) * c
+    tokens = _layout(layout) == STRIPED_TOKENS
+    rows = n if tokens else max(0, p_end - p_begin) * c
     o_dtype = q.dtype if o_dtype is None else o_dtype
     if out is None:
-        o = torch.empty((B, H, rows, d), dtype=o_dtype, device=dev)
-        lse = torch.empty((B, H, rows), dtype=torch.float32, device=dev) if want_lse else None
+        alloc = torch.zeros if tokens and (p_begin, p_end) != (0, P) else torch.empty
+        o = alloc((B, H, rows, d), dtype=o_dtype, device=dev)
+        lse = alloc((B, H, rows), dtype=torch.float32, device=dev) if want_lse else None
     else:
         o, lse = out
+        if o.shape != (B, H, rows, d) or o.dtype != o_dtype or not o.is_contiguous() or o.device != dev:
+            raise ValueError(f"out[0] must be a contiguous {o_dtype} tensor of shape {(B, H, rows, d)} on {dev}")
+        if lse is not None and (lse.shape != (B, H, rows) or lse.dtype != torch.float32
+                                or not lse.is_contiguous() or lse.device != dev):
+            raise ValueError(f"out[1] must be None or a contiguous float32 tensor of shape {(B, H, rows)} on {dev}")
     if stats is not None and (stats.dtype != torch.int64 or stats.numel() < P * P * 4 or not stats.is_contiguous()):
         raise ValueError("stats must be new_stats(P)")
     pr = _problem(B, H, n, d, P, _dtype_code(q.dtype), layout, causal, scale)

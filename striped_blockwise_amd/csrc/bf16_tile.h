@@ -108,8 +108,10 @@ __device__ __forceinline__ bf16x8 read_a_tr(const char* tile, int off_lo, int of
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// DMA of tiles of ROWS rows (row-major, 256 B per row) into LDS, split into 1 KB segments (4
-// rows) over NW wavefronts: wave w does segments w, w + NW, ...  Each wave keeps the per-lane
+// DMA of tiles of ROWS rows (256 B per row) into LDS, split into 1 KB segments (4 rows) over NW
+// wavefronts: wave w does segments w, w + NW, ...  In global memory consecutive rows of a block
+// are row_step rows apart (1 for a block stored on its own; P for a striped block read straight
+// from a token-order tensor, whose row y is token y P + k).  Each wave keeps the per-lane
 // offsets of its segments in `unsigned voff[DmaShape<NW, ROWS>::PER_WAVE]`: lane j of segment
 // seg fills LDS row 4 seg + j / 16 at physical chunk j % 16, which holds logical chunk
 // (j % 16) ^ mask(row) of that row (the XOR permutation is its own inverse).  The offsets pass as
@@ -123,25 +125,28 @@ struct DmaShape {
 };
 
 template <int NW, int ROWS>
-__device__ __forceinline__ void dma_init(unsigned* voff, Swz kind, int wave_u, int lane) {
+__device__ __forceinline__ void dma_init(unsigned* voff, Swz kind, int wave_u, int lane, int row_step) {
 #pragma unroll
   for (int i = 0; i < DmaShape<NW, ROWS>::PER_WAVE; ++i) {
     const int row = (wave_u + i * NW) * 4 + (lane >> 4);
     const int mask = kind == SWZ_K ? swz<SWZ_K>(row) : (kind == SWZ_V ? swz<SWZ_V>(row) : swz<SWZ_T>(row));
-    voff[i] = (unsigned)(row * ROWB + (((lane & 15) ^ mask) << 4));
+    voff[i] = (unsigned)row * (unsigned)row_step * ROWB + (unsigned)(((lane & 15) ^ mask) << 4);
   }
 }
 
-// Rows x0 .. x0 + ROWS - 1 of a block of c rows at `block` into the LDS tile `tile`.  The buffer
-// descriptor starts at row x0 and holds only the rows that exist, so the per-lane offsets are
-// loop constants and rows past the end of the block are out of range: the buffer unit returns
-// zeros for them, which land in LDS.
+// Rows x0 .. x0 + ROWS - 1 (x0 < c) of a block of c rows at `block` into the LDS tile `tile`.
+// The buffer descriptor starts at row x0 and ends after the last row that exists, so the
+// per-lane offsets are loop constants and rows past the end of the block are out of range: the
+// buffer unit returns zeros for them, which land in LDS.  (ROWS - 1) * row_step * 256 + 256 must
+// fit in 32 bits.
 template <int NW, int ROWS>
 __device__ __forceinline__ void dma_issue(const unsigned* voff, const char* block, char* tile, int x0, int c,
-                                          int wave_u) {
+                                          int row_step, int wave_u) {
   constexpr int SEGS = DmaShape<NW, ROWS>::SEGS;
+  const unsigned last = (unsigned)(min(c - x0, ROWS) - 1);
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(block + (int64_t)x0 * ROWB), 0, (c - x0) * ROWB, 0x00020000);
+      (void*)(block + (int64_t)x0 * row_step * ROWB), 0, (int)((last * (unsigned)row_step + 1) * ROWB),
+      0x00020000);
 #pragma unroll
   for (int i = 0; i < DmaShape<NW, ROWS>::PER_WAVE; ++i) {
     const int seg = wave_u + i * NW;

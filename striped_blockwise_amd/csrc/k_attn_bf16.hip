@@ -50,6 +50,13 @@ constexpr float TAU = 8.0f;     // lazy-rescale threshold, log2 units
 #ifndef RA_BF16_OCC
 #define RA_BF16_OCC 2           // target wavefronts per SIMD
 #endif
+#ifndef RA_BF16_SUB
+#define RA_BF16_SUB 1           // TK-key tiles per LDS stage (one DMA issue and one barrier each)
+#endif
+#ifndef RA_BF16_PRIO
+#define RA_BF16_PRIO 0          // 1: fixed issue priority wave % 3 (distinct on each SIMD)
+#endif
+constexpr int SUB = RA_BF16_SUB;
 
 // LDS layout of a K or V tile: row = key, 256 B = 16 chunks of 16 B with a per-row XOR mask on
 // the chunk index.  K tiles are only read row-wise (MFMA A operand), V tiles only transposed
@@ -61,7 +68,7 @@ struct Attn {
   static constexpr int TQ = NW * QW;              // query rows per workgroup
   static constexpr int KB = TK / 32;              // 32-key MFMA blocks per tile
   static constexpr int KS = TK / 16;              // 16-key MFMA k-steps per tile (P V)
-  static constexpr int TILE = TK * ROWB;          // bytes of one K or V tile
+  static constexpr int TILE = SUB * TK * ROWB;    // bytes of one K or V stage
 
   // Per-lane constant parts of the LDS addresses.
   int k_base[8];       // K operand: row l32, chunk (2 dk + hh)
@@ -91,6 +98,11 @@ __global__ __launch_bounds__(NT, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) {
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const int c = a.c;
+  if (RA_BF16_PRIO) {
+    const int pr = wave_u % 3;
+    if (pr == 1) __builtin_amdgcn_s_setprio(1);
+    else if (pr == 2) __builtin_amdgcn_s_setprio(2);
+  }
 
   // Block -> (stream = (device, head), q-tile).  Blocks are dispatched round-robin over the 8
   // XCDs (block i on XCD i % 8), each with its own L2.  XCD-major order gives XCD x the streams
@@ -119,19 +131,21 @@ __global__ __launch_bounds__(NT, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) {
 
   A off;
   off.init_offsets(lane);
-  unsigned kdma[DmaShape<NW, TK>::PER_WAVE], vdma[DmaShape<NW, TK>::PER_WAVE];
-  dma_init<NW, TK>(kdma, SWZ_K, wave_u, lane);
-  dma_init<NW, TK>(vdma, SWZ_V, wave_u, lane);
+  constexpr int SR = SUB * TK;                       // key rows per stage
+  unsigned kdma[DmaShape<NW, SR>::PER_WAVE], vdma[DmaShape<NW, SR>::PER_WAVE];
+  dma_init<NW, SR>(kdma, SWZ_K, wave_u, lane, a.row_step);
+  dma_init<NW, SR>(vdma, SWZ_V, wave_u, lane, a.row_step);
 
   // ---- Q columns (B operand): lane holds row qw0 + 32 qb + l32, head dims 16 dk + 8 hh .. +7
   const __bf16* qp = (const __bf16*)a.q + bh * a.q_bh_stride + dev * a.q_dev_stride;
+  const int64_t rstride = (int64_t)a.row_step * D;   // elements between rows of a block
   bf16x8 qf[QB][8];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = qw0 + qb * 32 + l32;
 #pragma unroll
     for (int dk = 0; dk < 8; ++dk)
-      qf[qb][dk] = row < c ? *reinterpret_cast<const bf16x8*>(qp + (int64_t)row * D + dk * 16 + hh * 8)
+      qf[qb][dk] = row < c ? *reinterpret_cast<const bf16x8*>(qp + row * rstride + dk * 16 + hh * 8)
                            : bf16x8{};
   }
 
@@ -286,30 +300,37 @@ __global__ __launch_bounds__(NT, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) {
     };
 
     if (ntk > 0) {
-      // tile t lives in stage t & 1; its DMA was issued one iteration earlier.  The loop is
-      // unrolled by two so that the stage offsets are compile-time immediates.
-      dma_issue<NW, TK>(kdma, kblk, kst(0), 0, c, wave_u);
-      dma_issue<NW, TK>(vdma, vblk, vst(0), 0, c, wave_u);
-      auto iter = [&](int t, auto stage_c) __attribute__((always_inline)) {
+      // stage u (tiles u*SUB .. u*SUB+SUB-1) lives in LDS stage u & 1; its DMA was issued one
+      // iteration earlier.  The loop is unrolled by two so that the stage offsets are
+      // compile-time immediates.
+      const int nst = (ntk + SUB - 1) / SUB;
+      dma_issue<NW, SR>(kdma, kblk, kst(0), 0, c, a.row_step, wave_u);
+      dma_issue<NW, SR>(vdma, vblk, vst(0), 0, c, a.row_step, wave_u);
+      auto iter = [&](int u, auto stage_c) __attribute__((always_inline)) {
         constexpr int S = decltype(stage_c)::value;
-        wait_dma_and_barrier();                       // tile t landed; the other stage is free
-        if (t + 1 < ntk) {
-          dma_issue<NW, TK>(kdma, kblk, smem + (1 - S) * TILE, (t + 1) * TK, c, wave_u);
-          dma_issue<NW, TK>(vdma, vblk, smem + (3 - S) * TILE, (t + 1) * TK, c, wave_u);
+        wait_dma_and_barrier();                       // stage u landed; the other one is free
+        if (u + 1 < nst) {
+          dma_issue<NW, SR>(kdma, kblk, smem + (1 - S) * TILE, (u + 1) * SR, c, a.row_step, wave_u);
+          dma_issue<NW, SR>(vdma, vblk, smem + (3 - S) * TILE, (u + 1) * SR, c, a.row_step, wave_u);
         }
-        const int cls = tile_class(t);
-        if (cls) {
-          compute_s(smem + S * TILE, sA);
-          if (cls >= 2) apply_mask(sA, t, cls == 2);
-          softmax_pv(sA, smem + (2 + S) * TILE);
+#pragma unroll
+        for (int sb = 0; sb < SUB; ++sb) {
+          const int t = u * SUB + sb;
+          if (SUB > 1 && t >= ntk) break;
+          const int cls = tile_class(t);
+          if (cls) {
+            compute_s(smem + S * TILE + sb * TK * ROWB, sA);
+            if (cls >= 2) apply_mask(sA, t, cls == 2);
+            softmax_pv(sA, smem + (2 + S) * TILE + sb * TK * ROWB);
+          }
         }
       };
-      int t = 0;
-      for (; t + 1 < ntk; t += 2) {
-        iter(t, std::integral_constant<int, 0>{});
-        iter(t + 1, std::integral_constant<int, 1>{});
+      int u = 0;
+      for (; u + 1 < nst; u += 2) {
+        iter(u, std::integral_constant<int, 0>{});
+        iter(u + 1, std::integral_constant<int, 1>{});
       }
-      if (t < ntk) iter(t, std::integral_constant<int, 0>{});
+      if (u < nst) iter(u, std::integral_constant<int, 0>{});
       __syncthreads();                                // LDS stages free for the next round
     }
 
@@ -335,9 +356,9 @@ __global__ __launch_bounds__(NT, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) {
     const float inv = live ? 1.f / lt : 0.f;
     const int y = qw0 + qb * 32 + l32;
     if (y < c) {
-      const int64_t orow = (int64_t)dev * c + y;
+      const int64_t oel = bh * a.o_bh_stride + dev * a.o_dev_stride + y * rstride;
       if (a.o_f32) {
-        float* op = (float*)a.o + bh * a.o_bh_stride + orow * D;
+        float* op = (float*)a.o + oel;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -347,7 +368,7 @@ __global__ __launch_bounds__(NT, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) {
             *reinterpret_cast<float4*>(op + 32 * db + 8 * g + 4 * hh) = w;
           }
       } else {
-        __bf16* op = (__bf16*)a.o + bh * a.o_bh_stride + orow * D;
+        __bf16* op = (__bf16*)a.o + oel;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -359,7 +380,7 @@ __global__ __launch_bounds__(NT, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) {
           }
       }
       if (a.lse && hh == 0)
-        a.lse[bh * a.lse_bh_stride + orow] = live ? (m[qb] + __log2f(lt)) * LN2 : -INFINITY;
+        a.lse[bh * a.lse_bh_stride + dev * a.lse_dev_stride + (int64_t)y * a.row_step] = live ? (m[qb] + __log2f(lt)) * LN2 : -INFINITY;
     }
   }
 }

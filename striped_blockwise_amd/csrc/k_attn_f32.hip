@@ -35,11 +35,12 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
   const int q_last = min(c, q0 + TQ) - 1;                  // last in-range row of the tile
 
   const float* qp = (const float*)a.q + bh * a.q_bh_stride + dev * a.q_dev_stride;
+  const int64_t rstride = (int64_t)a.row_step * D;        // elements between rows of a block
   float qv[D];
   const float qs = a.scale * LOG2E;
   if (y < c) {
 #pragma unroll
-    for (int j = 0; j < D; ++j) qv[j] = qp[(int64_t)y * D + j] * qs;
+    for (int j = 0; j < D; ++j) qv[j] = qp[y * rstride + j] * qs;
   } else {
 #pragma unroll
     for (int j = 0; j < D; ++j) qv[j] = 0.f;
@@ -70,8 +71,8 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
       for (int i = lane; i < TK * D / 4; i += 64) {
         const int row = x0 + i / (D / 4);
         const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-        sk[i] = row < c ? reinterpret_cast<const float4*>(kp + (int64_t)row * D)[i % (D / 4)] : z;
-        sv[i] = row < c ? reinterpret_cast<const float4*>(vp + (int64_t)row * D)[i % (D / 4)] : z;
+        sk[i] = row < c ? reinterpret_cast<const float4*>(kp + row * rstride)[i % (D / 4)] : z;
+        sv[i] = row < c ? reinterpret_cast<const float4*>(vp + row * rstride)[i % (D / 4)] : z;
       }
       __syncthreads();
       // tile class on its in-range part (same for every lane of the workgroup)
@@ -121,17 +122,17 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
   if (y < c) {
     const bool live = l > 0.f;
     const float inv = live ? 1.f / l : 0.f;
-    const int64_t orow = (int64_t)dev * c + y;
+    const int64_t oel = bh * a.o_bh_stride + dev * a.o_dev_stride + y * rstride;
     if (a.o_f32) {
-      float* op = (float*)a.o + bh * a.o_bh_stride + orow * D;
+      float* op = (float*)a.o + oel;
 #pragma unroll
       for (int e = 0; e < D; ++e) op[e] = acc[e] * inv;
     } else {
-      __bf16* op = (__bf16*)a.o + bh * a.o_bh_stride + orow * D;
+      __bf16* op = (__bf16*)a.o + oel;
 #pragma unroll
       for (int e = 0; e < D; ++e) op[e] = (__bf16)(acc[e] * inv);
     }
-    if (a.lse) a.lse[bh * a.lse_bh_stride + orow] = live ? (m + __log2f(l)) * LN2 : -INFINITY;
+    if (a.lse) a.lse[bh * a.lse_bh_stride + dev * a.lse_dev_stride + (int64_t)y * a.row_step] = live ? (m + __log2f(l)) * LN2 : -INFINITY;
   }
 }
 

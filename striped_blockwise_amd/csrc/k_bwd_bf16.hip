@@ -135,8 +135,8 @@ __global__ __launch_bounds__(RA_BWD_DQ_NW * 64, 2) void k_bwd_dq_bf16(BwdArgs a)
 #pragma unroll
     for (int sec = 0; sec < 2; ++sec) k_tr[db][sec] = a_tr_off<SWZ_T>(lane, db, sec);
   unsigned kdma[DmaShape<NW, TS>::PER_WAVE], vdma[DmaShape<NW, TS>::PER_WAVE];
-  dma_init<NW, TS>(kdma, SWZ_T, wave_u, lane);
-  dma_init<NW, TS>(vdma, SWZ_K, wave_u, lane);
+  dma_init<NW, TS>(kdma, SWZ_T, wave_u, lane, 1);
+  dma_init<NW, TS>(vdma, SWZ_K, wave_u, lane, 1);
 
   // B operands: this lane's query row of Q and dO, head dims 16 dk + 8 hh .. +7
   const __bf16* qp = (const __bf16*)a.q + bh * a.q_bh_stride + dev * a.q_dev_stride + (int64_t)y * D + hh * 8;
@@ -225,14 +225,14 @@ __global__ __launch_bounds__(RA_BWD_DQ_NW * 64, 2) void k_bwd_dq_bf16(BwdArgs a)
       }
     };
 
-    dma_issue<NW, TS>(kdma, kblk, smem, 0, c, wave_u);
-    dma_issue<NW, TS>(vdma, vblk, smem + 2 * TILE, 0, c, wave_u);
+    dma_issue<NW, TS>(kdma, kblk, smem, 0, c, 1, wave_u);
+    dma_issue<NW, TS>(vdma, vblk, smem + 2 * TILE, 0, c, 1, wave_u);
     auto iter = [&](int t, auto stage_c) __attribute__((always_inline)) {
       constexpr int S = decltype(stage_c)::value;
       wait_dma_and_barrier();                         // tile t landed; the other stage is free
       if (t + 1 < ntk) {
-        dma_issue<NW, TS>(kdma, kblk, smem + (1 - S) * TILE, (t + 1) * TS, c, wave_u);
-        dma_issue<NW, TS>(vdma, vblk, smem + (3 - S) * TILE, (t + 1) * TS, c, wave_u);
+        dma_issue<NW, TS>(kdma, kblk, smem + (1 - S) * TILE, (t + 1) * TS, c, 1, wave_u);
+        dma_issue<NW, TS>(vdma, vblk, smem + (3 - S) * TILE, (t + 1) * TS, c, 1, wave_u);
       }
       const int cls = tile_class(t);
       if (cls) compute(smem + S * TILE, smem + (2 + S) * TILE, t, cls == 2);
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(RA_BWD_DKV_NW * 64, 2) void k_bwd_dkv_bf16(BwdArgs 
   const int rw0 = a_rowwise_off<SWZ_T>(lane, 0);
   const int tr0 = a_tr_off<SWZ_T>(lane, 0, 0);
   unsigned dma[DmaShape<NW, TS>::PER_WAVE];
-  dma_init<NW, TS>(dma, SWZ_T, wave_u, lane);
+  dma_init<NW, TS>(dma, SWZ_T, wave_u, lane, 1);
 
   // B operands: this lane's key row of K and V
   const int64_t kvo = bh * a.kv_bh_stride + (int64_t)kvi * a.kv_blk_stride + (int64_t)x * D + hh * 8;
@@ -315,8 +315,8 @@ __global__ __launch_bounds__(RA_BWD_DKV_NW * 64, 2) void k_bwd_dkv_bf16(BwdArgs 
 
     auto issue = [&](int t, int S) __attribute__((always_inline)) {
       const int y0 = t * TS;
-      dma_issue<NW, TS>(dma, qblk, smem + S * TILE, y0, c, wave_u);
-      dma_issue<NW, TS>(dma, oblk, smem + (2 + S) * TILE, y0, c, wave_u);
+      dma_issue<NW, TS>(dma, qblk, smem + S * TILE, y0, c, 1, wave_u);
+      dma_issue<NW, TS>(dma, oblk, smem + (2 + S) * TILE, y0, c, 1, wave_u);
       if (wave_u == 0 && lane < 32) {
         // lane i < 32 copies L and D of row y0 + i to bytes 4 i of the stage's L and D areas;
         // rows past the block end read as 0

@@ -33,6 +33,10 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int64_t elem_bytes(int32_t dtype) { return dtype == RA_F32 ? 4 : 2; }
 
+// Largest P for RA_STRIPED_TOKENS: a K/V tile's rows are P rows apart, and a tile's span must
+// stay far inside the 32-bit range of a buffer descriptor.
+constexpr int32_t kMaxTokenP = 65536;
+
 bool empty_problem(const ra_problem_t* pr) { return pr->B == 0 || pr->H == 0 || pr->n == 0; }
 
 // Problem-level checks shared by every attention entry point.
@@ -44,8 +48,10 @@ ra_status_t check_problem(const ra_problem_t* pr) {
   if (pr->n % pr->P != 0)
     return fail(RA_E_INVAL, "n (%lld) must be a multiple of P (%d)", (long long)pr->n, pr->P);
   if (pr->dtype != RA_BF16 && pr->dtype != RA_F32) return fail(RA_E_INVAL, "unknown dtype %d", pr->dtype);
-  if (pr->layout != RA_CONTIGUOUS && pr->layout != RA_STRIPED)
+  if (pr->layout != RA_CONTIGUOUS && pr->layout != RA_STRIPED && pr->layout != RA_STRIPED_TOKENS)
     return fail(RA_E_INVAL, "unknown layout %d", pr->layout);
+  if (pr->layout == RA_STRIPED_TOKENS && pr->P > kMaxTokenP)
+    return fail(RA_E_INVAL, "RA_STRIPED_TOKENS needs P <= %d (got %d)", kMaxTokenP, pr->P);
   if (pr->causal != 0 && pr->causal != 1) return fail(RA_E_INVAL, "causal must be 0 or 1");
   if (!std::isfinite(pr->scale)) return fail(RA_E_INVAL, "scale must be finite");
   const int64_t c = pr->n / pr->P;
@@ -58,6 +64,14 @@ ra_status_t check_problem(const ra_problem_t* pr) {
   if (!sup)
     return fail(RA_E_UNSUPPORTED, "head dim %lld is not supported for %s inputs (bf16: 128; f32: 32, 64, 128)",
                 (long long)pr->d, pr->dtype == RA_BF16 ? "bf16" : "f32");
+  return ok();
+}
+
+// The per-round entry points take one block per pointer, with its rows back to back.
+ra_status_t check_block_layout(const ra_problem_t* pr) {
+  if (pr->layout == RA_STRIPED_TOKENS)
+    return fail(RA_E_UNSUPPORTED, "per-round entry points take blocks in layout order: use RA_STRIPED "
+                                  "(rows permuted by ra_permute)");
   return ok();
 }
 
@@ -163,7 +177,8 @@ ra_status_t ra_permute_rope(const void* src, void* dst, const int64_t* pos, int6
   if (BH < 0 || n < 0) return fail(RA_E_INVAL, "BH and n must be >= 0");
   if (d <= 0 || d % 2) return fail(RA_E_INVAL, "head dim d must be positive and even (got %lld)", (long long)d);
   if (dtype != RA_BF16 && dtype != RA_F32) return fail(RA_E_INVAL, "unknown dtype %d", dtype);
-  if (layout != RA_CONTIGUOUS && layout != RA_STRIPED) return fail(RA_E_INVAL, "unknown layout %d", layout);
+  if (layout != RA_CONTIGUOUS && layout != RA_STRIPED && layout != RA_STRIPED_TOKENS)
+    return fail(RA_E_INVAL, "unknown layout %d", layout);
   if (style != RA_ROPE_INTERLEAVED && style != RA_ROPE_HALF) return fail(RA_E_INVAL, "unknown RoPE style %d", style);
   if (!(base > 0.0) || !std::isfinite(base)) return fail(RA_E_INVAL, "base must be positive and finite");
   if (P < 1) return fail(RA_E_INVAL, "P must be >= 1 (got %d)", P);
@@ -188,6 +203,8 @@ ra_status_t ra_round(const ra_problem_t* prob, const void* q, const void* k, con
                      float* o_part, float* lse_part, ra_round_stats_t* stats, void* stream) {
   ra_status_t st = ra_check(prob, p, kv);
   if (st != RA_OK) return st;
+  st = check_block_layout(prob);
+  if (st != RA_OK) return st;
   if (empty_problem(prob)) return ok();
   const int64_t c = prob->n / prob->P;
   const int64_t d = prob->d;
@@ -204,8 +221,10 @@ ra_status_t ra_round(const ra_problem_t* prob, const void* q, const void* k, con
   a.q = q; a.k = k; a.v = v;
   a.q_bh_stride = q_stride_bh; a.kv_bh_stride = kv_stride_bh;
   a.q_dev_stride = 0; a.kv_blk_stride = 0;
+  a.row_step = 1;
   a.o = o_part; a.lse = lse_part;
   a.o_bh_stride = c * d; a.lse_bh_stride = c;
+  a.o_dev_stride = c * d; a.lse_dev_stride = c;
   a.c = (int)c; a.P = prob->P; a.BH = (int)(prob->B * prob->H);
   a.p_begin = p; a.n_dev = 1; a.kv_base = kv;
   a.r_begin = ra::ring_block(p, kv, prob->P);   // (p - kv) mod P: the round that brings block kv
@@ -256,16 +275,28 @@ ra_status_t ra_forward(const ra_problem_t* prob, const void* q, const void* k, c
   if (stats && !aligned(stats, 8)) return fail(RA_E_INVAL, "stats must be 8-byte aligned");
   const int64_t ndev = p_end - p_begin;
   ra::AttnArgs a{};
-  a.q = (const char*)q + (int64_t)p_begin * c * d * elem_bytes(prob->dtype);
   a.k = k; a.v = v;
   a.q_bh_stride = prob->n * d; a.kv_bh_stride = prob->n * d;
-  a.q_dev_stride = c * d; a.kv_blk_stride = c * d;
-  a.o = o; a.lse = lse;
-  a.o_bh_stride = ndev * c * d; a.lse_bh_stride = ndev * c;
+  a.lse = lse;
+  if (prob->layout == RA_STRIPED_TOKENS) {
+    // Row y of device p's block is token y * P + p of the token-order tensors.
+    a.q = (const char*)q + (int64_t)p_begin * d * elem_bytes(prob->dtype);
+    a.q_dev_stride = d; a.kv_blk_stride = d; a.row_step = prob->P;
+    a.o = (char*)o + (int64_t)p_begin * d * (o_dtype == RA_F32 ? 4 : 2);
+    if (lse) a.lse = lse + p_begin;
+    a.o_bh_stride = prob->n * d; a.lse_bh_stride = prob->n;
+    a.o_dev_stride = d; a.lse_dev_stride = 1;
+  } else {
+    a.q = (const char*)q + (int64_t)p_begin * c * d * elem_bytes(prob->dtype);
+    a.q_dev_stride = c * d; a.kv_blk_stride = c * d; a.row_step = 1;
+    a.o = o;
+    a.o_bh_stride = ndev * c * d; a.lse_bh_stride = ndev * c;
+    a.o_dev_stride = c * d; a.lse_dev_stride = c;
+  }
   a.c = (int)c; a.P = prob->P; a.BH = (int)(prob->B * prob->H);
   a.p_begin = p_begin; a.n_dev = (int)ndev; a.kv_base = 0;
   a.r_begin = 0; a.r_count = prob->P;
-  a.layout = prob->layout; a.causal = prob->causal;
+  a.layout = prob->layout == RA_CONTIGUOUS ? RA_CONTIGUOUS : RA_STRIPED; a.causal = prob->causal;
   a.scale = eff_scale(prob);
   a.o_f32 = o_dtype == RA_F32 ? 1 : 0;
   a.stats = stats; a.stats_single = 0;
@@ -298,6 +329,8 @@ ra_status_t ra_backward_round(const ra_problem_t* prob, const void* q, const voi
                               int64_t kv_stride_bh, int64_t row_stride_bh, int32_t p, int32_t kv,
                               float* dq_acc, float* dk_acc, float* dv_acc, void* stream) {
   ra_status_t st = ra_check(prob, p, kv);
+  if (st != RA_OK) return st;
+  st = check_block_layout(prob);
   if (st != RA_OK) return st;
   st = check_bwd_support(prob);
   if (st != RA_OK) return st;
@@ -341,6 +374,8 @@ ra_status_t ra_backward(const ra_problem_t* prob, const void* q, const void* k, 
                         const void* dout, const float* lse, const float* delta, int32_t p_begin,
                         int32_t p_end, float* dq, float* dk, float* dv, void* stream) {
   ra_status_t st = check_problem(prob);
+  if (st != RA_OK) return st;
+  st = check_block_layout(prob);
   if (st != RA_OK) return st;
   st = check_bwd_support(prob);
   if (st != RA_OK) return st;

@@ -39,10 +39,14 @@ struct AttnArgs {
   int64_t kv_bh_stride;   // same for k and v
   int64_t q_dev_stride;   // elements between consecutive device blocks of q
   int64_t kv_blk_stride;  // elements between consecutive K/V blocks
+  int row_step;           // rows between consecutive rows of a block in q, k, v, o and lse: 1,
+                          // or P for a striped block read from a token-order tensor
   void* o;                // output rows of device p_begin, then p_begin+1, ...
   float* lse;             // nullable
   int64_t o_bh_stride;    // elements between (b, h) matrices of o
+  int64_t o_dev_stride;   // elements between the first rows of consecutive devices in o
   int64_t lse_bh_stride;  // elements between (b, h) vectors of lse
+  int64_t lse_dev_stride; // same for lse
   int c;                  // rows per block
   int P;                  // devices
   int BH;                 // B * H

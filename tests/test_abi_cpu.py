@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(ra):
 
 
 def test_abi_version_and_tiles(ra):
-    assert ra.abi_version() == 3
+    assert ra.abi_version() == 4
     tq, tk = ra.tile_shape(ra.BF16, 128)
     assert tq > 0 and tk > 0 and tq % 32 == 0 and tk % 16 == 0
     assert ra.tile_shape(ra.F32, 64)[0] > 0
@@ -63,7 +63,8 @@ def test_abi_version_and_tiles(ra):
     (dict(d=96), NotImplementedError, "head dim 96"),
     (dict(d=0), ValueError, "head dim d"),
     (dict(dtype=5), ValueError, "dtype"),
-    (dict(layout=2), ValueError, "layout"),
+    (dict(layout=3), ValueError, "layout"),
+    (dict(layout=2, n=1 << 17, P=1 << 17), ValueError, "P <= 65536"),
     (dict(scale=float("nan")), ValueError, "scale"),
     (dict(B=-1), ValueError, ">= 0"),
     (dict(n=1 << 40, P=1), ValueError, "too large"),
@@ -80,7 +81,7 @@ def test_check_accepts_every_workload(ra):
     import workloads
     for w in workloads.WORKLOADS.values():
         dt = ra.F32 if w.dtype == "f32" else ra.BF16
-        for layout in (ra.CONTIGUOUS, ra.STRIPED):
+        for layout in (ra.CONTIGUOUS, ra.STRIPED, ra.STRIPED_TOKENS):
             ra.check(w.B, w.H, w.n, w.d, w.P, dt, layout, True, 0.0, p=w.P - 1, kv=0)
     ra.check(0, 8, 0, 128, 4)            # empty problems are valid
 
@@ -131,6 +132,21 @@ def test_backward_host_validation(ra):
     assert L.ra_backward_round(ctypes.byref(empty), *args13, 0, 0, 0, 0, 1, 0, N, N, N, N) == 0
 
 
+def test_token_order_layout_host_validation(ra):
+    """RA_STRIPED_TOKENS is accepted by ra_forward's validation and refused (unsupported, nothing
+    launched) by the per-round and backward entry points."""
+    L = ra.lib()
+    N = None
+    pr = ra._problem(1, 1, 256, 128, 4, ra.BF16, ra.STRIPED_TOKENS, True, 0.0)
+    assert L.ra_check(ctypes.byref(pr), 3, 1) == 0
+    assert L.ra_forward(ctypes.byref(pr), N, N, N, 0, 4, N, ra.BF16, N, N, N) == -1     # NULL, not layout
+    assert b"NULL" in L.ra_last_error()
+    assert L.ra_round(ctypes.byref(pr), N, N, N, 0, 0, 0, 0, N, N, N, N) == -2
+    assert b"layout order" in L.ra_last_error()
+    assert L.ra_backward(ctypes.byref(pr), *(N,) * 6, 0, 4, N, N, N, N) == -2
+    assert L.ra_backward_round(ctypes.byref(pr), *(N,) * 6, 0, 0, 0, 0, 1, 0, N, N, N, N) == -2
+
+
 def test_rope_host_validation(ra):
     L = ra.lib()
     N = None
@@ -145,6 +161,8 @@ def test_rope_host_validation(ra):
     assert L.ra_permute_rope(*args(n=18)) == -1 and b"multiple of P" in L.ra_last_error()
     assert L.ra_permute_rope(*args(base=-1.0)) == -1
     assert L.ra_permute_rope(*args(dtype=9)) == -1
+    assert L.ra_permute_rope(*args(layout=3)) == -1 and b"layout" in L.ra_last_error()
+    assert L.ra_permute_rope(*args(layout=ra.STRIPED_TOKENS)) == -1 and b"NULL" in L.ra_last_error()
 
 
 def test_binding_refuses_cpu_tensors(ra):

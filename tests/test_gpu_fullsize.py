@@ -1,8 +1,8 @@
 """GPU parity at full workload sizes, in the launch configuration bench.py times.
 
 * 256K-token share (n = 262144, P = 8, H = 32, d = 128, bf16): device 7's query block against all
-  8 K/V blocks with ra_forward, contiguous and striped (the striped inputs go through
-  ra_permute first, as in the timed step).  Every device of both layouts is also run once, so
+  8 K/V blocks with ra_forward, contiguous and striped (the striped inputs through ra_permute
+  first), and striped read straight from the token-order tensors, as in the timed step.  Every device of both layouts is also run once, so
   the whole sequence's striped output, un-permuted on the GPU, can be compared with the
   contiguous one.
 * The backward of device 7's share (ra_backward), both layouts: dQ on sampled rows against the
@@ -111,6 +111,30 @@ def test_share256k_device7(ra, share, layout):
     compare(_sel(o, heads, rows).float(), _sel(lse, heads, rows), o_ref, l_ref, "bf16",
             f"share256k {layout} device {p}")
     del qs, ks, vs
+
+
+def test_share256k_device7_token_order(ra, share):
+    """The timed step: device 7's share read straight from the token-order tensors
+    (RA_STRIPED_TOKENS).  Bit-exact against the permuted path, sampled rows against the oracle."""
+    w, q, k, v = share
+    P, c, p = w.P, w.c, w.device
+    stats = ra.new_stats(P)
+    o, lse = ra.forward(q, k, v, P, "striped_tokens", True, p_begin=p, p_end=p + 1, stats=stats)
+    qs, ks, vs = (ra.permute(t, P) for t in (q, k, v))
+    o_s, l_s = ra.forward(qs, ks, vs, P, "striped", True, p_begin=p, p_end=p + 1)
+    del qs, ks, vs
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, :, p::P], o_s) and torch.equal(lse[:, :, p::P], l_s), "token order vs permuted"
+    tq, tk = ra.tile_shape(ra.BF16, w.d)
+    got = stats.cpu().numpy()
+    assert np.array_equal(got[p], _expected_stats_row("striped", P, c, p, w.B * w.H, tq, tk)), got[p]
+    rows = _sample_rows(c, seed=99)
+    heads = [3, 17, 30]
+    tokens = rows * P + p
+    o_ref, l_ref = _oracle_rows(w, heads, tokens)
+    compare(_sel(o, heads, tokens).float(), _sel(lse, heads, tokens), o_ref, l_ref, "bf16",
+            "share256k token order device 7")
+    del o, lse, o_s, l_s
 
 
 def test_share256k_whole_sequence_equivariance(ra, share):

@@ -1,0 +1,131 @@
+"""GPU parity of the token-order striped layout (RA_STRIPED_TOKENS) of ra_forward.
+
+The partition, ring schedule and GetMask are those of the striped layout (Striped Attention
+review, "分区策略对比" and "GetMask 函数"); only the addressing differs: the kernels read and write
+row y of device p's block at token y*P + p of token-order tensors, so no permutation pass runs.
+Checked here:
+* against the fp64 oracle's attention in token order (natural positions), element by element,
+  at sizes that span several tiles and a ragged tail, for bf16 and f32 inputs;
+* bit-exact against the permuted path (ra_permute, ra_forward on RA_STRIPED, inverse ra_permute
+  of O and LSE): both run the same arithmetic in the same order on the same values;
+* the work counters equal the striped layout's closed forms;
+* a device range writes only its own rows (token t with p_begin <= t mod P < p_end).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import attention as OA
+from oracle import ring as OR
+from tests._gpu_util import compare, need_gpu, np64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ra():
+    need_gpu()
+    import striped_blockwise_amd as m
+    return m
+
+
+def _expected_stats(P, c, BH, causal, tq, tk, devices):
+    exp = np.zeros((P, P, 4), dtype=np.int64)
+    for p in devices:
+        for r in range(P):
+            kk = OR.kv_block(p, r, P)
+            pairs = OR.work_closed_form("striped", p, kk, c, causal)
+            full, diag, skip = OR.tile_counts_closed_form("striped", p, kk, c, tq, tk, causal)
+            exp[p, r] = [pairs * BH, full * BH, diag * BH, skip * BH]
+    return exp
+
+
+def _permuted_path(ra, q, k, v, P, causal, o_dtype):
+    qs, ks, vs = (ra.permute(t, P) for t in (q, k, v))
+    o, lse = ra.forward(qs, ks, vs, P, "striped", causal, o_dtype=o_dtype)
+    return ra.permute(o, P, inverse=True), ra.permute(lse, P, dim=-1, inverse=True)
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64), (torch.float32, 128)])
+@pytest.mark.parametrize("P,c", [(4, 1), (4, 37), (8, 200), (3, 512), (1, 300), (64, 1)])
+def test_token_order_matches_oracle(ra, dtype, d, P, c):
+    B, H = 1, 2
+    n = P * c
+    g = torch.Generator().manual_seed(1000 + 7 * c + P + d)
+    q, k, v = (torch.randn((B, H, n, d), generator=g).mul(0.5).to(dtype) for _ in range(3))
+    o_ref, l_ref = OA.attention(q, k, v, True)                     # token order, positions 0..n-1
+    kind = "f32" if dtype == torch.float32 else "bf16"
+    qg, kg, vg = (t.cuda() for t in (q, k, v))
+    stats = ra.new_stats(P)
+    o, lse = ra.forward(qg, kg, vg, P, "striped_tokens", True, o_dtype=torch.float32, stats=stats)
+    torch.cuda.synchronize()
+    compare(o, lse, o_ref, l_ref, kind, f"token order P={P} c={c} {dtype}")
+    tq, tk = ra.tile_shape(ra.F32 if kind == "f32" else ra.BF16, d)
+    assert np.array_equal(stats.cpu().numpy(), _expected_stats(P, c, B * H, True, tq, tk, range(P)))
+    o_p, l_p = _permuted_path(ra, qg, kg, vg, P, True, torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_p) and torch.equal(lse, l_p), "token order differs from the permuted path"
+
+
+def test_token_order_seq8k_bf16(ra):
+    w = workloads.get("seq_n8k")
+    q, k, v = workloads.qkv(w)
+    o_ref, l_ref = OA.attention(q, k, v, True)
+    qg, kg, vg = (t.cuda() for t in (q, k, v))
+    for o_dtype in (torch.float32, torch.bfloat16):
+        o, lse = ra.forward(qg, kg, vg, w.P, "striped_tokens", True, o_dtype=o_dtype)
+        torch.cuda.synchronize()
+        compare(o.float(), lse, o_ref, l_ref, "bf16", f"seq8k token order, {o_dtype} out")
+        o_p, l_p = _permuted_path(ra, qg, kg, vg, w.P, True, o_dtype)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_p) and torch.equal(lse, l_p)
+
+
+def test_token_order_not_causal(ra):
+    P, c, H = 4, 100, 2
+    g = torch.Generator().manual_seed(77)
+    q, k, v = (torch.randn((1, H, P * c, 128), generator=g).to(torch.bfloat16) for _ in range(3))
+    o_ref, l_ref = OA.attention(q, k, v, False)
+    o, lse = ra.forward(q.cuda(), k.cuda(), v.cuda(), P, "striped_tokens", False, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    compare(o, lse, o_ref, l_ref, "bf16", "token order, no mask")
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64)])
+def test_token_order_device_range_writes_only_its_rows(ra, dtype, d):
+    P, c, H = 4, 130, 2
+    n = P * c
+    g = torch.Generator().manual_seed(5 + d)
+    q, k, v = (torch.randn((1, H, n, d), generator=g).to(dtype) for _ in range(3))
+    o_ref, l_ref = OA.attention(q, k, v, True)
+    kind = "f32" if dtype == torch.float32 else "bf16"
+    o = torch.full((1, H, n, d), float("nan"), device="cuda")
+    lse = torch.full((1, H, n), float("nan"), device="cuda")
+    stats = ra.new_stats(P)
+    ra.forward(q.cuda(), k.cuda(), v.cuda(), P, "striped_tokens", True, p_begin=1, p_end=3,
+               o_dtype=torch.float32, stats=stats, out=(o, lse))
+    torch.cuda.synchronize()
+    mine = np.isin(np.arange(n) % P, [1, 2])
+    on, ln = np64(o), np64(lse)
+    assert np.isnan(on[:, :, ~mine]).all() and np.isnan(ln[:, :, ~mine]).all(), "rows of other devices written"
+    compare(on[:, :, mine], ln[:, :, mine], o_ref[:, :, mine], l_ref[:, :, mine], kind, "device range 1..3")
+    tq, tk = ra.tile_shape(ra.F32 if kind == "f32" else ra.BF16, d)
+    assert np.array_equal(stats.cpu().numpy(), _expected_stats(P, c, H, True, tq, tk, [1, 2]))
+    # out=None allocates zeros for the rows outside the range
+    o2, l2 = ra.forward(q.cuda(), k.cuda(), v.cuda(), P, "striped_tokens", True, p_begin=1, p_end=3,
+                        o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert not np64(o2)[:, :, ~mine].any() and not np64(l2)[:, :, ~mine].any()
+    assert torch.equal(o2[:, :, torch.from_numpy(mine).cuda()], o[:, :, torch.from_numpy(mine).cuda()])
+
+
+def test_token_order_rejected_where_unsupported(ra):
+    x = torch.zeros((1, 1, 256, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(NotImplementedError, match="layout order"):
+        ra.round(x[:, :, :64], x[:, :, :64], x[:, :, :64], 4, 1, 0, "striped_tokens", True)
+    o = torch.empty((1, 1, 128, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="out\\[0\\]"):                     # o must hold all n rows
+        ra.forward(x, x, x, 4, "striped_tokens", True, p_begin=0, p_end=2, out=(o, None))
