@@ -50,13 +50,9 @@ constexpr float TAU = 8.0f;     // lazy-rescale threshold, log2 units
 #ifndef RA_BF16_OCC
 #define RA_BF16_OCC 2           // target wavefronts per SIMD
 #endif
-#ifndef RA_BF16_SUB
-#define RA_BF16_SUB 1           // TK-key tiles per LDS stage (one DMA issue and one barrier each)
-#endif
 #ifndef RA_BF16_PRIO
-#define RA_BF16_PRIO 0          // 1: fixed issue priority wave % 3 (distinct on each SIMD)
+#define RA_BF16_PRIO 1          // 1: fixed issue priority wave % 3 (distinct on each SIMD)
 #endif
-constexpr int SUB = RA_BF16_SUB;
 
 // LDS layout of a K or V tile: row = key, 256 B = 16 chunks of 16 B with a per-row XOR mask on
 // the chunk index.  K tiles are only read row-wise (MFMA A operand), V tiles only transposed
@@ -68,7 +64,7 @@ struct Attn {
   static constexpr int TQ = NW * QW;              // query rows per workgroup
   static constexpr int KB = TK / 32;              // 32-key MFMA blocks per tile
   static constexpr int KS = TK / 16;              // 16-key MFMA k-steps per tile (P V)
-  static constexpr int TILE = SUB * TK * ROWB;    // bytes of one K or V stage
+  static constexpr int TILE = TK * ROWB;          // bytes of one K or V tile
 
   // Per-lane constant parts of the LDS addresses.
   int k_base[8];       // K operand: row l32, chunk (2 dk + hh)
@@ -98,6 +94,10 @@ __global__ __launch_bounds__(NT, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) {
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const int c = a.c;
+  // The three wavefronts that share a SIMD get distinct fixed issue priorities (wave % 3 differs
+  // for w, w + 4, w + 8 as well as for three consecutive waves), so that after each tile's
+  // barrier they do not contend symmetrically for the matrix core but run staggered; measured
+  // 1.2% faster than equal priorities.
   if (RA_BF16_PRIO) {
     const int pr = wave_u % 3;
     if (pr == 1) __builtin_amdgcn_s_setprio(1);
@@ -131,10 +131,9 @@ __global__ __launch_bounds__(NT, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) {
 
   A off;
   off.init_offsets(lane);
-  constexpr int SR = SUB * TK;                       // key rows per stage
-  unsigned kdma[DmaShape<NW, SR>::PER_WAVE], vdma[DmaShape<NW, SR>::PER_WAVE];
-  dma_init<NW, SR>(kdma, SWZ_K, wave_u, lane, a.row_step);
-  dma_init<NW, SR>(vdma, SWZ_V, wave_u, lane, a.row_step);
+  unsigned kdma[DmaShape<NW, TK>::PER_WAVE], vdma[DmaShape<NW, TK>::PER_WAVE];
+  dma_init<NW, TK>(kdma, SWZ_K, wave_u, lane, a.row_step);
+  dma_init<NW, TK>(vdma, SWZ_V, wave_u, lane, a.row_step);
 
   // ---- Q columns (B operand): lane holds row qw0 + 32 qb + l32, head dims 16 dk + 8 hh .. +7
   const __bf16* qp = (const __bf16*)a.q + bh * a.q_bh_stride + dev * a.q_dev_stride;
@@ -300,37 +299,30 @@ __global__ __launch_bounds__(NT, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) {
     };
 
     if (ntk > 0) {
-      // stage u (tiles u*SUB .. u*SUB+SUB-1) lives in LDS stage u & 1; its DMA was issued one
-      // iteration earlier.  The loop is unrolled by two so that the stage offsets are
-      // compile-time immediates.
-      const int nst = (ntk + SUB - 1) / SUB;
-      dma_issue<NW, SR>(kdma, kblk, kst(0), 0, c, a.row_step, wave_u);
-      dma_issue<NW, SR>(vdma, vblk, vst(0), 0, c, a.row_step, wave_u);
-      auto iter = [&](int u, auto stage_c) __attribute__((always_inline)) {
+      // tile t lives in stage t & 1; its DMA was issued one iteration earlier.  The loop is
+      // unrolled by two so that the stage offsets are compile-time immediates.
+      dma_issue<NW, TK>(kdma, kblk, kst(0), 0, c, a.row_step, wave_u);
+      dma_issue<NW, TK>(vdma, vblk, vst(0), 0, c, a.row_step, wave_u);
+      auto iter = [&](int t, auto stage_c) __attribute__((always_inline)) {
         constexpr int S = decltype(stage_c)::value;
-        wait_dma_and_barrier();                       // stage u landed; the other one is free
-        if (u + 1 < nst) {
-          dma_issue<NW, SR>(kdma, kblk, smem + (1 - S) * TILE, (u + 1) * SR, c, a.row_step, wave_u);
-          dma_issue<NW, SR>(vdma, vblk, smem + (3 - S) * TILE, (u + 1) * SR, c, a.row_step, wave_u);
+        wait_dma_and_barrier();                       // tile t landed; the other stage is free
+        if (t + 1 < ntk) {
+          dma_issue<NW, TK>(kdma, kblk, smem + (1 - S) * TILE, (t + 1) * TK, c, a.row_step, wave_u);
+          dma_issue<NW, TK>(vdma, vblk, smem + (3 - S) * TILE, (t + 1) * TK, c, a.row_step, wave_u);
         }
-#pragma unroll
-        for (int sb = 0; sb < SUB; ++sb) {
-          const int t = u * SUB + sb;
-          if (SUB > 1 && t >= ntk) break;
-          const int cls = tile_class(t);
-          if (cls) {
-            compute_s(smem + S * TILE + sb * TK * ROWB, sA);
-            if (cls >= 2) apply_mask(sA, t, cls == 2);
-            softmax_pv(sA, smem + (2 + S) * TILE + sb * TK * ROWB);
-          }
+        const int cls = tile_class(t);
+        if (cls) {
+          compute_s(smem + S * TILE, sA);
+          if (cls >= 2) apply_mask(sA, t, cls == 2);
+          softmax_pv(sA, smem + (2 + S) * TILE);
         }
       };
-      int u = 0;
-      for (; u + 1 < nst; u += 2) {
-        iter(u, std::integral_constant<int, 0>{});
-        iter(u + 1, std::integral_constant<int, 1>{});
+      int t = 0;
+      for (; t + 1 < ntk; t += 2) {
+        iter(t, std::integral_constant<int, 0>{});
+        iter(t + 1, std::integral_constant<int, 1>{});
       }
-      if (u < nst) iter(u, std::integral_constant<int, 0>{});
+      if (t < ntk) iter(t, std::integral_constant<int, 0>{});
       __syncthreads();                                // LDS stages free for the next round
     }
 
