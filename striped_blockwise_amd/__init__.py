@@ -120,6 +120,20 @@ def _gpu(*ts: torch.Tensor):
     return dev
 
 
+def _check_out(t, shape, dtype, dev, name: str) -> None:
+    """A caller-provided output must be exactly what the kernels write: the library checks sizes
+    from the problem, not from the tensor, so a smaller buffer would be overrun."""
+    if (not isinstance(t, torch.Tensor) or tuple(t.shape) != tuple(shape) or t.dtype != dtype
+            or not t.is_contiguous() or t.device != dev):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on {dev}")
+
+
+def _check_stats(stats, numel: int, dev) -> None:
+    if stats is not None and (stats.dtype != torch.int64 or stats.numel() < numel or not stats.is_contiguous()
+                              or stats.device != dev):
+        raise ValueError(f"stats must be a contiguous int64 tensor of >= {numel} elements on {dev}")
+
+
 def _stream(dev) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
 
@@ -176,8 +190,9 @@ def permute_ids(ids: torch.Tensor, P: int, inverse: bool = False, out=None) -> t
     _gpu(ids)
     if ids.dtype != torch.int64 or ids.dim() != 1 or not ids.is_contiguous():
         raise ValueError("ids must be a contiguous 1-D int64 tensor")
-    out = torch.empty_like(ids) if out is None else out
-    _gpu(ids, out)
+    if out is None:
+        out = torch.empty_like(ids)
+    _check_out(out, ids.shape, torch.int64, ids.device, "out")
     with torch.cuda.device(ids.device):
         _raise(lib().ra_permute_ids(_ptr(ids), _ptr(out), ids.numel(), int(P), 1 if inverse else 0,
                                     _vp(_stream(ids.device))), "ra_permute_ids")
@@ -224,8 +239,9 @@ def round(q_blk, k_blk, v_blk, P: int, p: int, kv: int, layout="contiguous", cau
         lse = torch.empty((B, H, c), dtype=torch.float32, device=dev)
     else:
         o, lse = out
-    if stats is not None and (stats.dtype != torch.int64 or stats.numel() < 4 or not stats.is_contiguous()):
-        raise ValueError("stats must be a contiguous int64 tensor of >= 4 elements")
+        _check_out(o, (B, H, c, d), torch.float32, dev, "out[0]")
+        _check_out(lse, (B, H, c), torch.float32, dev, "out[1]")
+    _check_stats(stats, 4, dev)
     pr = _problem(B, H, c * P, d, P, _dtype_code(q_blk.dtype), layout, causal, scale)
     with torch.cuda.device(dev):
         _raise(lib().ra_round(ctypes.byref(pr), _ptr(q_blk), _ptr(k_blk), _ptr(v_blk), sq, sk,
@@ -279,13 +295,10 @@ def forward(q, k, v, P: int, layout="contiguous", causal=True, p_begin: int = 0,
         lse = alloc((B, H, rows), dtype=torch.float32, device=dev) if want_lse else None
     else:
         o, lse = out
-        if o.shape != (B, H, rows, d) or o.dtype != o_dtype or not o.is_contiguous() or o.device != dev:
-            raise ValueError(f"out[0] must be a contiguous {o_dtype} tensor of shape {(B, H, rows, d)} on {dev}")
-        if lse is not None and (lse.shape != (B, H, rows) or lse.dtype != torch.float32
-                                or not lse.is_contiguous() or lse.device != dev):
-            raise ValueError(f"out[1] must be None or a contiguous float32 tensor of shape {(B, H, rows)} on {dev}")
-    if stats is not None and (stats.dtype != torch.int64 or stats.numel() < P * P * 4 or not stats.is_contiguous()):
-        raise ValueError("stats must be new_stats(P)")
+        _check_out(o, (B, H, rows, d), o_dtype, dev, "out[0]")
+        if lse is not None:
+            _check_out(lse, (B, H, rows), torch.float32, dev, "out[1]")
+    _check_stats(stats, P * P * 4, dev)
     pr = _problem(B, H, n, d, P, _dtype_code(q.dtype), layout, causal, scale)
     with torch.cuda.device(dev):
         _raise(lib().ra_forward(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), int(p_begin), int(p_end),
@@ -317,8 +330,8 @@ def bwd_delta(o: torch.Tensor, dout: torch.Tensor, out=None) -> torch.Tensor:
     rows = o.numel() // d if d else 0
     if out is None:
         out = torch.empty(o.shape[:-1], dtype=torch.float32, device=o.device)
-    elif out.shape != o.shape[:-1] or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 tensor of shape o.shape[:-1]")
+    else:
+        _check_out(out, o.shape[:-1], torch.float32, o.device, "out")
     with torch.cuda.device(o.device):
         _raise(lib().ra_bwd_delta(_ptr(o), _dtype_code(o.dtype), _ptr(dout), _dtype_code(dout.dtype), rows, d,
                                   _ptr(out), _vp(_stream(o.device))), "ra_bwd_delta")
@@ -349,10 +362,10 @@ def backward_round(q_blk, k_blk, v_blk, dout_blk, lse_blk, delta_blk, P: int, p:
         raise ValueError("lse and delta must be [B, H, c] with the same (b, h) stride")
     if grads is None:
         grads = tuple(torch.zeros((B, H, c, d), dtype=torch.float32, device=dev) for _ in range(3))
-    for g in grads:
-        if g.shape != (B, H, c, d) or g.dtype != torch.float32 or not g.is_contiguous():
-            raise ValueError("gradient accumulators must be contiguous float32 [B, H, c, d]")
-    _gpu(q_blk, *grads)
+    if len(grads) != 3:
+        raise ValueError("grads must be (dq_acc, dk_acc, dv_acc)")
+    for g, name in zip(grads, ("dq_acc", "dk_acc", "dv_acc")):
+        _check_out(g, (B, H, c, d), torch.float32, dev, name)
     pr = _problem(B, H, c * P, d, P, _dtype_code(q_blk.dtype), layout, causal, scale)
     with torch.cuda.device(dev):
         _raise(lib().ra_backward_round(ctypes.byref(pr), _ptr(q_blk), _ptr(k_blk), _ptr(v_blk), _ptr(dout_blk),
@@ -397,6 +410,9 @@ def backward(q, k, v, dout, lse, P: int, layout="contiguous", causal=True, p_beg
         dv = torch.empty((B, H, n, d), dtype=torch.float32, device=dev)
     else:
         dq, dk, dv = out
+        _check_out(dq, (B, H, m, d), torch.float32, dev, "out[0] (dq)")
+        _check_out(dk, (B, H, n, d), torch.float32, dev, "out[1] (dk)")
+        _check_out(dv, (B, H, n, d), torch.float32, dev, "out[2] (dv)")
     _gpu(q, dq, dk, dv, delta)
     pr = _problem(B, H, n, d, P, _dtype_code(q.dtype), layout, causal, scale)
     with torch.cuda.device(dev):

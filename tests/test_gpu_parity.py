@@ -310,3 +310,37 @@ def test_invalid_arguments_raise_before_launch(ra):
         ra.forward(x, x, x, 4, "contiguous", True)               # unsupported head dim
     with pytest.raises(ValueError):
         ra.forward(q, q, q, 4, "contiguous", True, p_begin=3, p_end=3)
+
+
+def test_wrong_outputs_raise_before_launch(ra):
+    """Caller-provided outputs whose shape, dtype or device differ from what the kernels write are
+    refused on the host (the library sizes its writes from the problem, not from the buffers)."""
+    n, P, d = 256, 4, 128
+    c = n // P
+    q = torch.zeros((1, 2, n, d), dtype=torch.bfloat16, device="cuda")
+    small = torch.empty((1, 2, c - 1, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((1, 2, c), device="cuda")
+    with pytest.raises(ValueError, match="out\\[0\\]"):
+        ra.forward(q, q, q, P, "striped", True, p_begin=1, p_end=2, out=(small, lse))
+    with pytest.raises(ValueError, match="out\\[1\\]"):
+        ra.forward(q, q, q, P, "striped", True, p_begin=1, p_end=2,
+                   out=(torch.empty((1, 2, c, d), dtype=torch.bfloat16, device="cuda"), lse[:, :, :-1]))
+    with pytest.raises(ValueError, match="stats"):
+        ra.forward(q, q, q, P, "striped", True, stats=torch.zeros((P, P, 4), dtype=torch.int64))     # on the CPU
+    blk = q[:, :, :c]
+    with pytest.raises(ValueError, match="out\\[0\\]"):
+        ra.round(blk, blk, blk, P, 1, 0, "striped", True,
+                 out=(torch.empty((1, 2, c, d), dtype=torch.bfloat16, device="cuda"), lse))   # o must be f32
+    with pytest.raises(ValueError, match="out"):
+        ra.permute_ids(torch.arange(n, device="cuda"), P, out=torch.empty(n - 1, dtype=torch.int64, device="cuda"))
+    o = torch.zeros((1, 2, c, d), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="out"):
+        ra.bwd_delta(o, o, out=torch.empty((1, 2, c)))                                             # on the CPU
+    dq = torch.empty((1, 2, c, d), device="cuda")
+    dkv = torch.empty((1, 2, n, d), device="cuda")
+    with pytest.raises(ValueError, match="dk"):
+        ra.backward(q, q, q, o, lse, P, "striped", True, 1, 2, delta=lse, out=(dq, dkv[:, :, :-1], dkv))
+    with pytest.raises(ValueError, match="dq_acc"):
+        ra.backward_round(blk, blk, blk, blk, lse, lse, P, 1, 0, "striped", True,
+                          grads=(dq[:, :1], dq, dq))
+    torch.cuda.synchronize()
