@@ -19,6 +19,8 @@ Also measured in the same run (reported as extra fields, never as ``value``):
     position IDs, then ra_forward on the permuted tensors (RA_STRIPED);
   * the streamed path: 8 x (ra_round + ra_merge), with merge and permute GB/s;
   * backward: ra_backward (dQ, dK, dV) of the same share in both layouts, useful TFLOP/s;
+  * the 8K-token sequence (P = 4): every (device, round) ra_round, and per round the slowest
+    device's time in both layouts (the emulated ring's round time) and their ratio;
   * roofline of the dominant kernel (the fused bf16 forward) against the bf16 MFMA peak;
   * cpu_baseline: the fp64 CPU oracle on a bounded sample of the same share.
 
@@ -118,12 +120,69 @@ def cpu_baseline(w, layout: str, budget_s: float = 12.0):
         heads += 1
         if elapsed >= budget_s:
             break
+    full = 4.0 * d * w.B * w.H * sum(OR.work_closed_form(layout, p, OR.kv_block(p, r, P), c, True) for r in range(P))
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:  # pragma: no cover
+        pass
     return {
         "value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
         "sample": f"{heads} head(s) x 256 evenly spaced query rows of device {p} ({layout}) against "
                   f"all {w.n} keys, fp64 NumPy; {flops:.3e} useful flops in {elapsed:.2f} s",
-        "host_cpus": os.cpu_count(),
+        "extrapolated_full_share_s": round(full / (flops / elapsed), 1),
+        "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": model,
     }
+
+
+def per_round_all_devices(torch, ra, dev, name: str = "seq_n8k", reps: int = 5):
+    """Emulated ring rounds of a whole small sequence: every (device p, round r) ra_round timed
+    alone (HIP events, a 512 MB write between reps so that no K/V block is served from cache),
+    median over reps; a round of the emulated ring lasts as long as its slowest device."""
+    import statistics
+
+    import workloads
+    from oracle import ring as OR
+    w = workloads.get(name)
+    P, c = w.P, w.c
+    q, k, v = (t.to(dev) for t in workloads.qkv(w))
+    lay = {"contiguous": (q, k, v), "striped": tuple(ra.permute(t, P) for t in (q, k, v))}
+    flush = torch.empty(128 * 2 ** 20, dtype=torch.float32, device=dev)
+    out = (torch.empty((w.B, w.H, c, w.d), dtype=torch.float32, device=dev),
+           torch.empty((w.B, w.H, c), dtype=torch.float32, device=dev))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {}
+    for layout, (qq, kk, vv) in lay.items():
+        tmax = []
+        for r in range(P):
+            per_dev = []
+            for p in range(P):
+                kb = OR.kv_block(p, r, P)
+                args_r = (qq[:, :, p * c:(p + 1) * c], kk[:, :, kb * c:(kb + 1) * c], vv[:, :, kb * c:(kb + 1) * c],
+                          P, p, kb, layout, True)
+                ts = []
+                for _ in range(reps + 1):
+                    flush.fill_(1.0)
+                    a.record()
+                    ra.round(*args_r, out=out)
+                    b.record()
+                    torch.cuda.synchronize()
+                    ts.append(a.elapsed_time(b))
+                per_dev.append(statistics.median(ts[1:]))
+            tmax.append(max(per_dev))
+        res[layout] = tmax
+    ideal = []
+    for r in range(P):
+        pc = max(OR.work_closed_form("contiguous", p, OR.kv_block(p, r, P), c, True) for p in range(P))
+        ps = max(OR.work_closed_form("striped", p, OR.kv_block(p, r, P), c, True) for p in range(P))
+        ideal.append(round(pc / ps, 5))
+    del flush, lay, q, k, v
+    return {"workload": name, "n": w.n, "P": P, "H": w.H, "reps": reps,
+            "round_max_ms_contiguous": [round(x, 4) for x in res["contiguous"]],
+            "round_max_ms_striped": [round(x, 4) for x in res["striped"]],
+            "speedup_striped_over_ring": [round(x / y, 4) for x, y in zip(res["contiguous"], res["striped"])],
+            "ideal_speedup": ideal}
 
 
 def sweep(torch, ra, dev, P: int = 8, H: int = 8, d: int = 128,
@@ -457,6 +516,9 @@ def main(argv=None) -> int:
 
     if not args.no_extras:
         result["backward"] = backward_leg(torch, ra, w, (qs, ks, vs), (q, k, v), flops_s, flops_c, p)
+        result["per_round_all_devices"] = per_round_all_devices(torch, ra, dev)
+        log("[bench] seq_n8k per-round speedup (slowest device) "
+            + " ".join(f"{x:.3f}" for x in result["per_round_all_devices"]["speedup_striped_over_ring"]))
 
     if not args.no_extras:
         # context: a plain library GEMM (torch.matmul -> hipBLASLt), bf16, square 8192, on the

@@ -34,11 +34,12 @@ using namespace bf16t;
 #ifndef RA_BF16_NW
 #define RA_BF16_NW 12           // wavefronts per workgroup (one workgroup fills a CU at 3 waves per SIMD)
 #endif
+#ifndef RA_BF16_NW_SMALL
+#define RA_BF16_NW_SMALL 4      // wavefronts per workgroup for grids that do not fill the chip
+#endif
 #ifndef RA_BF16_XMAP
 #define RA_BF16_XMAP 1          // 1: XCD-major block order (one (head, device) stream per XCD)
 #endif
-constexpr int NW = RA_BF16_NW;  // wavefronts per workgroup
-constexpr int NT = NW * 64;     // threads per workgroup
 constexpr float TAU = 8.0f;     // lazy-rescale threshold, log2 units
 
 #ifndef RA_BF16_QB
@@ -62,7 +63,7 @@ constexpr float TAU = 8.0f;     // lazy-rescale threshold, log2 units
 // the chunk index.  K tiles are only read row-wise (MFMA A operand), V tiles only transposed
 // (ds_read_b64_tr_b16), so each gets the mask that is conflict-free for its own read pattern.
 
-template <int QB, int TK, bool STATS>
+template <int QB, int TK, bool STATS, int NW>
 struct Attn {
   static constexpr int QW = 32 * QB;              // query rows per wavefront
   static constexpr int TQ = NW * QW;              // query rows per workgroup
@@ -84,9 +85,9 @@ struct Attn {
   }
 };
 
-template <int QB, int TK, bool STATS>
-__global__ __launch_bounds__(NT, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) {
-  using A = Attn<QB, TK, STATS>;
+template <int QB, int TK, bool STATS, int NW>
+__global__ __launch_bounds__(NW * 64, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) {
+  using A = Attn<QB, TK, STATS, NW>;
   constexpr int QW = A::QW, TQ = A::TQ, KB = A::KB, KS = A::KS, TILE = A::TILE;
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];   // K0 K1 V0 V1
   auto kst = [&](int i) __attribute__((always_inline)) { return smem + (i & 1) * TILE; };
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(NT, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) {
   // for w, w + 4, w + 8 as well as for three consecutive waves), so that after each tile's
   // barrier they do not contend symmetrically for the matrix core but run staggered; measured
   // 1.2% faster than equal priorities.
-  if (RA_BF16_PRIO) {
+  if (RA_BF16_PRIO && NW % 3 == 0) {
     const int pr = wave_u % 3;
     if (pr == 1) __builtin_amdgcn_s_setprio(1);
     else if (pr == 2) __builtin_amdgcn_s_setprio(2);
@@ -407,19 +408,47 @@ constexpr int TK_SEL = RA_BF16_TK;
 bool attn_bf16_supported(int64_t d) { return d == D; }
 void attn_bf16_tile(int* tq, int* tk) { *tq = 32 * QB_SEL; *tk = TK_SEL; }
 
-hipError_t launch_attn_bf16(const AttnArgs& a, int d, hipStream_t s) {
-  if (d != D) return hipErrorInvalidValue;
+namespace {
+
+// Compute units of the current device (queried once per device).
+int cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <int NW>
+hipError_t launch_nw(const AttnArgs& a, hipStream_t s) {
   constexpr int TQ = NW * 32 * QB_SEL;
   const int64_t blocks = (int64_t)((a.c + TQ - 1) / TQ) * a.BH * a.n_dev;
-  if (blocks * NT >= (1ll << 32)) return hipErrorInvalidConfiguration;
+  if (blocks * NW * 64 >= (1ll << 32)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks);
   AttnArgs b = a;
   b.xcd_major = ((int64_t)a.BH * a.n_dev) % 8 == 0 ? 1 : 0;
   if (a.stats)
-    hipLaunchKernelGGL((k_attn_bf16<QB_SEL, TK_SEL, true>), grid, dim3(NT), 0, s, b);
+    hipLaunchKernelGGL((k_attn_bf16<QB_SEL, TK_SEL, true, NW>), grid, dim3(NW * 64), 0, s, b);
   else
-    hipLaunchKernelGGL((k_attn_bf16<QB_SEL, TK_SEL, false>), grid, dim3(NT), 0, s, b);
+    hipLaunchKernelGGL((k_attn_bf16<QB_SEL, TK_SEL, false, NW>), grid, dim3(NW * 64), 0, s, b);
   return hipGetLastError();
+}
+
+}  // namespace
+
+// Wide workgroups (one per CU, 384 queries sharing each K/V tile) when the grid has at least
+// two of them per CU; otherwise the round lasts as long as one workgroup's sweep over its key
+// tiles, and 4-wave workgroups (one wave per SIMD) sweep about three times faster.
+hipError_t launch_attn_bf16(const AttnArgs& a, int d, hipStream_t s) {
+  if (d != D) return hipErrorInvalidValue;
+  constexpr int TQW = RA_BF16_NW * 32 * QB_SEL;
+  const int64_t wide = (int64_t)((a.c + TQW - 1) / TQW) * a.BH * a.n_dev;
+  if (wide >= 2 * (int64_t)cu_count()) return launch_nw<RA_BF16_NW>(a, s);
+  return launch_nw<RA_BF16_NW_SMALL>(a, s);
 }
 
 }  // namespace ra

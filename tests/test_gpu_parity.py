@@ -344,3 +344,42 @@ def test_wrong_outputs_raise_before_launch(ra):
         ra.backward_round(blk, blk, blk, blk, lse, lse, P, 1, 0, "striped", True,
                           grads=(dq[:, :1], dq, dq))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "striped_tokens"])
+def test_wide_workgroup_path(ra, layout):
+    """A grid large enough for the 12-wave workgroups (at least two per CU: 128 heads x 2 devices
+    x 4 query tiles of 384 rows), with ragged query and key tiles (c = 1500).  Element-wise on 8
+    heads against the oracle, counters on all of them, and one round per direction."""
+    B, H, P, c, d = 1, 128, 2, 1500, 128
+    n = P * c
+    g = torch.Generator().manual_seed(2024)
+    q, k, v = (torch.randn((B, H, n, d), generator=g).mul(0.5).to(torch.bfloat16) for _ in range(3))
+    heads = [0, 1, 2, 3, 124, 125, 126, 127]
+    base = "striped" if layout == "striped_tokens" else layout
+    qh, kh, vh = (t[:, heads] for t in (q, k, v))
+    if layout == "striped_tokens":
+        o_ref, l_ref = OA.attention(qh, kh, vh, True)
+    else:
+        (ql, kl, vl), order = _oracle_layout((qh, kh, vh), P, layout)
+        o_ref, l_ref = OA.attention(ql, kl, vl, True, pos_q=order, pos_k=order)
+    qg, kg, vg = (ra.permute(t.cuda(), P) if layout == "striped" else t.cuda() for t in (q, k, v))
+    stats = ra.new_stats(P)
+    o, lse = ra.forward(qg, kg, vg, P, layout, True, o_dtype=torch.float32, stats=stats)
+    torch.cuda.synchronize()
+    idx = torch.tensor(heads, device="cuda")
+    compare(o.index_select(1, idx), lse.index_select(1, idx), o_ref, l_ref, "bf16", f"wide {layout}")
+    tq, tk = ra.tile_shape(ra.BF16, d)
+    assert np.array_equal(stats.cpu().numpy(), _expected_stats(base, P, c, B * H, True, tq, tk))
+    if layout == "striped_tokens":
+        return
+    (ql, kl, vl), _ = _oracle_layout((qh, kh, vh), P, layout)
+    for p, kk in ((1, 0), (0, 1), (1, 1)):
+        po, pl = ra.round(qg[:, :, p * c:(p + 1) * c], kg[:, :, kk * c:(kk + 1) * c], vg[:, :, kk * c:(kk + 1) * c],
+                          P, p, kk, layout, True)
+        torch.cuda.synchronize()
+        for j, h in enumerate(heads[::3]):
+            jj = heads.index(h)
+            ro, rl = OR.round_partial(ql[0, jj, p * c:(p + 1) * c], kl[0, jj, kk * c:(kk + 1) * c],
+                                      vl[0, jj, kk * c:(kk + 1) * c], layout, p, kk, True)
+            compare(po[0, h], pl[0, h], ro, rl, "bf16", f"wide round p={p} kv={kk} h={h}")
