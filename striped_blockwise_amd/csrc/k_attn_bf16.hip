@@ -18,9 +18,11 @@
 //   O^T += V^T P^T on MFMA: A = V^T, read from the row-major V tile with ds_read_b64_tr_b16
 //   (which transposes 4x4 blocks of 16-bit elements across lanes), B = P straight from the
 //   score registers (the contraction index is permuted identically on both operands).
-// The running max is only raised when a tile's max exceeds it by more than 2^8 (in exp2
-// units), so the rescale of O (64-128 multiplies per lane) is rare; the result is exact either
-// way because O, l and the reference max always stay consistent.
+// The running max is only raised when a tile's max exceeds it by more than 8 (in log2 units),
+// so the rescale of O (64-128 multiplies per lane) is rare; the result is exact either way
+// because O, l and the reference max always stay consistent.  The tile max itself is only
+// computed when P against the current reference comes out large (a lane's partial row sum
+// above 2^12) or a row has no reference yet; otherwise that first P is kept.
 #include <type_traits>
 
 #include "bf16_tile.h"
@@ -41,6 +43,11 @@ using namespace bf16t;
 #define RA_BF16_XMAP 1          // 1: XCD-major block order (one (head, device) stream per XCD)
 #endif
 constexpr float TAU = 8.0f;     // lazy-rescale threshold, log2 units
+#ifndef RA_BF16_LAZYMAX
+#define RA_BF16_LAZYMAX 1       // 1: skip the tile max unless P against the current reference gets large
+#endif
+constexpr bool LAZYMAX = RA_BF16_LAZYMAX != 0;
+constexpr float LAZY_LIM = 4096.0f;   // 2^(TAU + 4)
 
 #ifndef RA_BF16_QB
 #define RA_BF16_QB 1            // 32-query column blocks per wavefront
@@ -52,7 +59,7 @@ constexpr float TAU = 8.0f;     // lazy-rescale threshold, log2 units
 #define RA_BF16_OCC 2           // target wavefronts per SIMD
 #endif
 #ifndef RA_BF16_VPRE
-#define RA_BF16_VPRE 2          // V^T fragments: 0 read next to each MFMA, 1 all read before the P V MFMAs,
+#define RA_BF16_VPRE 3          // V^T fragments: 0 read next to each MFMA, 1 all read before the P V MFMAs,
                                 // 2 all before the softmax, 3 the first 16 keys' before the softmax
 #endif
 #ifndef RA_BF16_PRIO
@@ -162,9 +169,9 @@ __global__ __launch_bounds__(NW * 64, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) { m[qb] = -INFINITY; l[qb] = 0.f; }
   const float cs = a.scale * LOG2E;
-  // When the V^T fragments are read (see RA_BF16_VPRE).  Reading all of them before the softmax
-  // lets their LDS latency pass under the exp work, at the price of a few spilled registers;
-  // measured 1% faster than reading each next to its MFMA.  The counting variant, which holds
+  // When the V^T fragments are read (see RA_BF16_VPRE).  Reading the first 16 keys' fragments
+  // before the softmax lets their LDS latency pass under the exp work; all of them would need
+  // more registers than the 3-waves-per-SIMD budget leaves.  The counting variant, which holds
   // more registers and is never timed, keeps the reads next to the MFMAs.
   constexpr int VPRE = STATS ? 0 : RA_BF16_VPRE;
 
@@ -205,57 +212,86 @@ __global__ __launch_bounds__(NW * 64, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) 
     };
     if (VPRE == 2) read_v(0, KS);
     if (VPRE == 3) read_v(0, 1);
-    // row max and lazy rescale
-    float ref[QB];
-    bool any_grow = false;
-    float mt[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = s[qb][0][0];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int rg = 0; rg < 16; ++rg) mx = fmaxf(mx, s[qb][kb][rg]);
-      mt[qb] = pair_max(mx) * cs;
-      any_grow |= mt[qb] > m[qb] + TAU;
-    }
-    if (__builtin_amdgcn_ballot_w64(any_grow)) {
+    // Row max and lazy rescale: the reference m of a row is raised only when the tile's max
+    // exceeds it by more than TAU (log2 units).
+    auto grow_max = [&]() __attribute__((always_inline)) {
+      bool any_grow = false;
+      float mt[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const bool grow = mt[qb] > m[qb] + TAU;
-        const float m_new = grow ? mt[qb] : m[qb];
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m[qb] - m_new) : 1.0f;
-        l[qb] *= alpha;
+        float mx = s[qb][0][0];
 #pragma unroll
-        for (int db = 0; db < 4; ++db) o[qb][db] *= alpha;
-        m[qb] = m_new;
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int rg = 0; rg < 16; ++rg) mx = fmaxf(mx, s[qb][kb][rg]);
+        mt[qb] = pair_max(mx) * cs;
+        any_grow |= mt[qb] > m[qb] + TAU;
       }
-    }
+      if (__builtin_amdgcn_ballot_w64(any_grow)) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) ref[qb] = m[qb] == -INFINITY ? 0.f : m[qb];
-    // P = exp2(S * cs - ref) -> bf16, row sums of the rounded values
-    bf16x8 pf[QB][KS];
+        for (int qb = 0; qb < QB; ++qb) {
+          const bool grow = mt[qb] > m[qb] + TAU;
+          const float m_new = grow ? mt[qb] : m[qb];
+          const float alpha = grow ? __builtin_amdgcn_exp2f(m[qb] - m_new) : 1.0f;
+          l[qb] *= alpha;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          bf16x8 pk;
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][half * 8 + e], cs, -ref[qb]));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][half * 8 + e + 1], cs, -ref[qb]));
-            const bf16x2 pp = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
-            rs += p0 + p1;
-            pk[e] = pp[0];
-            pk[e + 1] = pp[1];
-          }
-          pf[qb][2 * kb + half] = pk;
+          for (int db = 0; db < 4; ++db) o[qb][db] *= alpha;
+          m[qb] = m_new;
         }
-      l[qb] += rs;
+      }
+    };
+    // P = exp2(S * cs - ref) -> bf16, and this lane's row sums of the unrounded values
+    bf16x8 pf[QB][KS];
+    float rsum[QB];
+    auto make_p = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float ref = m[qb] == -INFINITY ? 0.f : m[qb];
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            bf16x8 pk;
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              const float p0 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][half * 8 + e], cs, -ref));
+              const float p1 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][half * 8 + e + 1], cs, -ref));
+              const bf16x2 pp = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+              rs += p0 + p1;
+              pk[e] = pp[0];
+              pk[e + 1] = pp[1];
+            }
+            pf[qb][2 * kb + half] = pk;
+          }
+        rsum[qb] = rs;
+      }
+    };
+    if (LAZYMAX) {
+      // Without the tile max: P against the current reference, and the max path only when a
+      // row has no reference yet or a lane's sum shows a value above 2^(TAU + 4) (each of the
+      // lane's 16 values is at most its sum).  Either way O, l and m stay consistent.
+      bool first = false;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) first |= m[qb] == -INFINITY;
+      bool need_max = __builtin_amdgcn_ballot_w64(first) != 0;
+      if (!need_max) {
+        make_p();
+        bool big = false;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) big |= !(rsum[qb] <= LAZY_LIM);
+        need_max = __builtin_amdgcn_ballot_w64(big) != 0;
+      }
+      if (need_max) {
+        grow_max();
+        make_p();
+      }
+    } else {
+      grow_max();
+      make_p();
     }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l[qb] += rsum[qb];
     // O^T += V^T P^T
     if (VPRE == 1) read_v(0, KS);
     if (VPRE == 3) read_v(1, KS);

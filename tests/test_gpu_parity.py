@@ -383,3 +383,30 @@ def test_wide_workgroup_path(ra, layout):
             ro, rl = OR.round_partial(ql[0, jj, p * c:(p + 1) * c], kl[0, jj, kk * c:(kk + 1) * c],
                                       vl[0, jj, kk * c:(kk + 1) * c], layout, p, kk, True)
             compare(po[0, h], pl[0, h], ro, rl, "bf16", f"wide round p={p} kv={kk} h={h}")
+
+
+@pytest.mark.parametrize("H", [2, 128])          # 4-wave and 12-wave workgroups
+def test_rising_scores_take_the_rescale_path(ra, H):
+    """Scores that grow with the key position by about 3 log2 units per 32-key tile (more for
+    some heads), so that the running reference falls behind again and again and the kernel's
+    max-and-rescale path runs in the middle of the sweep, not only on a row's first tile."""
+    B, P, c, d = 1, 2, 768, 128
+    n = P * c
+    g = torch.Generator().manual_seed(99)
+    q = torch.randn((B, H, n, d), generator=g).mul(0.1)
+    k = torch.randn((B, H, n, d), generator=g).mul(0.1)
+    v = torch.randn((B, H, n, d), generator=g)
+    rate = torch.linspace(0.5, 2.0, H).view(1, H, 1)           # per-head growth factor
+    q[..., 0] = 8.0
+    k[..., 0] = 0.092 * rate * torch.arange(n, dtype=torch.float32).view(1, 1, n)
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    heads = [0, 1] if H == 2 else [0, 1, 63, 127]
+    for layout in ("contiguous", "striped"):
+        qh, kh, vh = (t[:, heads] for t in (q, k, v))
+        (ql, kl, vl), order = _oracle_layout((qh, kh, vh), P, layout)
+        o_ref, l_ref = OA.attention(ql, kl, vl, True, pos_q=order, pos_k=order)
+        qg, kg, vg = (ra.permute(t.cuda(), P) if layout == "striped" else t.cuda() for t in (q, k, v))
+        o, lse = ra.forward(qg, kg, vg, P, layout, True, o_dtype=torch.float32)
+        torch.cuda.synchronize()
+        idx = torch.tensor(heads, device="cuda")
+        compare(o.index_select(1, idx), lse.index_select(1, idx), o_ref, l_ref, "bf16", f"rising H={H} {layout}")
