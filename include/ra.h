@@ -66,8 +66,9 @@ enum {
                              ra_permute)                                                          */
   RA_STRIPED_TOKENS = 2   /* the partition and masks of RA_STRIPED, with the tensors left in token
                              order: row y of device p's block is token row y*P + p, and the
-                             kernels apply the permutation in their addressing.  ra_forward and
-                             ra_permute_rope (identity permutation) only; P <= 65536.            */
+                             kernels apply the permutation in their addressing.  ra_forward,
+                             ra_backward and ra_permute_rope (identity permutation) only;
+                             P <= 65536.                                                          */
 };
 
 /* One attention problem.  Plain host struct, passed by pointer. */
@@ -228,6 +229,9 @@ ra_status_t ra_backward_round(const ra_problem_t* prob, const void* q, const voi
  *   dq:      [B, H, m, d] float32, written
  *   dk, dv:  [B, H, n, d] float32, written: the gradient that the queries of devices
  *            p_begin..p_end-1 send to every key (the full gradient when the range is 0..P)
+ *   RA_STRIPED_TOKENS: every tensor in token order, with m = n: dout and dq [B, H, n, d],
+ *            lse and delta [B, H, n]; dq is written only on the rows of the selected devices
+ *            (tokens t with p_begin <= t mod P < p_end), dk and dv on every row.
  * Every output element is written exactly once, by one workgroup, in a fixed order. */
 ra_status_t ra_backward(const ra_problem_t* prob, const void* q, const void* k, const void* v,
                         const void* dout, const float* lse, const float* delta, int32_t p_begin,

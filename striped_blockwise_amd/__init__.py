@@ -7,8 +7,8 @@ fallback: if libra.so is missing or the tensors are not on a GPU the calls raise
 Layout names: "contiguous" (device p owns tokens [p*c, (p+1)*c); Ring Attention review, step 1)
 and "striped" (device p owns tokens p, p+P, ...; Striped Attention review, "分区策略对比"), with
 the rows permuted into layout order by ``permute``; "striped_tokens" is the striped partition
-with the tensors left in token order (``forward`` and ``permute_rope`` only): the kernels read
-and write row y of device p's block at token y*P + p.
+with the tensors left in token order (``forward``, ``backward`` and ``permute_rope`` only): the
+kernels read and write row y of device p's block at token y*P + p.
 """
 from __future__ import annotations
 
@@ -384,6 +384,9 @@ def backward(q, k, v, dout, lse, P: int, layout="contiguous", causal=True, p_beg
     bwd_delta, or None with o (forward's output) given to compute it.  Returns float32
     (dq [B, H, m, d], dk [B, H, n, d], dv [B, H, n, d]); dk and dv hold what the queries of
     the device range send to every key.
+    layout "striped_tokens": all tensors in token order and m = n (dout, dq [B, H, n, d]; lse,
+    delta [B, H, n]); dq rows of devices outside the range are left as they were (zeros when
+    out is None).
     """
     dev = _gpu(q, k, v, dout, lse)
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
@@ -395,7 +398,8 @@ def backward(q, k, v, dout, lse, P: int, layout="contiguous", causal=True, p_beg
     B, H, n, d = q.shape
     p_end = P if p_end is None else p_end
     c = n // P if P > 0 else 0
-    m = max(0, p_end - p_begin) * c
+    tokens = _layout(layout) == STRIPED_TOKENS
+    m = n if tokens else max(0, p_end - p_begin) * c
     if dout.shape != (B, H, m, d) or lse.shape != (B, H, m) or lse.dtype != torch.float32:
         raise ValueError(f"dout must be [B, H, {m}, d] and lse float32 [B, H, {m}]")
     if delta is None:
@@ -405,7 +409,8 @@ def backward(q, k, v, dout, lse, P: int, layout="contiguous", causal=True, p_beg
     if delta.shape != (B, H, m) or delta.dtype != torch.float32 or not delta.is_contiguous():
         raise ValueError(f"delta must be contiguous float32 [B, H, {m}]")
     if out is None:
-        dq = torch.empty((B, H, m, d), dtype=torch.float32, device=dev)
+        dq = (torch.zeros if tokens and (p_begin, p_end) != (0, P) else torch.empty)(
+            (B, H, m, d), dtype=torch.float32, device=dev)
         dk = torch.empty((B, H, n, d), dtype=torch.float32, device=dev)
         dv = torch.empty((B, H, n, d), dtype=torch.float32, device=dev)
     else:

@@ -135,12 +135,13 @@ __global__ __launch_bounds__(RA_BWD_DQ_NW * 64, 2) void k_bwd_dq_bf16(BwdArgs a)
 #pragma unroll
     for (int sec = 0; sec < 2; ++sec) k_tr[db][sec] = a_tr_off<SWZ_T>(lane, db, sec);
   unsigned kdma[DmaShape<NW, TS>::PER_WAVE], vdma[DmaShape<NW, TS>::PER_WAVE];
-  dma_init<NW, TS>(kdma, SWZ_T, wave_u, lane, 1);
-  dma_init<NW, TS>(vdma, SWZ_K, wave_u, lane, 1);
+  dma_init<NW, TS>(kdma, SWZ_T, wave_u, lane, a.row_step);
+  dma_init<NW, TS>(vdma, SWZ_K, wave_u, lane, a.row_step);
 
   // B operands: this lane's query row of Q and dO, head dims 16 dk + 8 hh .. +7
-  const __bf16* qp = (const __bf16*)a.q + bh * a.q_bh_stride + dev * a.q_dev_stride + (int64_t)y * D + hh * 8;
-  const __bf16* dop = (const __bf16*)a.dout + bh * a.do_bh_stride + dev * a.do_dev_stride + (int64_t)y * D + hh * 8;
+  const int64_t rstride = (int64_t)a.row_step * D;   // elements between rows of a block
+  const __bf16* qp = (const __bf16*)a.q + bh * a.q_bh_stride + dev * a.q_dev_stride + y * rstride + hh * 8;
+  const __bf16* dop = (const __bf16*)a.dout + bh * a.do_bh_stride + dev * a.do_dev_stride + y * rstride + hh * 8;
   bf16x8 qf[8], df[8];
 #pragma unroll
   for (int dk = 0; dk < 8; ++dk) {
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(RA_BWD_DQ_NW * 64, 2) void k_bwd_dq_bf16(BwdArgs a)
   }
   float nl = 0.f, dl = 0.f;    // -L log2(e) and D of this lane's row
   if (y < c) {
-    const int64_t ro = bh * a.row_bh_stride + dev * a.row_dev_stride + y;
+    const int64_t ro = bh * a.row_bh_stride + dev * a.row_dev_stride + (int64_t)y * a.row_step;
     nl = -fmaxf(a.lse[ro], NEG_BIG) * LOG2E;
     dl = a.delta[ro];
   }
@@ -225,14 +226,14 @@ __global__ __launch_bounds__(RA_BWD_DQ_NW * 64, 2) void k_bwd_dq_bf16(BwdArgs a)
       }
     };
 
-    dma_issue<NW, TS>(kdma, kblk, smem, 0, c, 1, wave_u);
-    dma_issue<NW, TS>(vdma, vblk, smem + 2 * TILE, 0, c, 1, wave_u);
+    dma_issue<NW, TS>(kdma, kblk, smem, 0, c, a.row_step, wave_u);
+    dma_issue<NW, TS>(vdma, vblk, smem + 2 * TILE, 0, c, a.row_step, wave_u);
     auto iter = [&](int t, auto stage_c) __attribute__((always_inline)) {
       constexpr int S = decltype(stage_c)::value;
       wait_dma_and_barrier();                         // tile t landed; the other stage is free
       if (t + 1 < ntk) {
-        dma_issue<NW, TS>(kdma, kblk, smem + (1 - S) * TILE, (t + 1) * TS, c, 1, wave_u);
-        dma_issue<NW, TS>(vdma, vblk, smem + (3 - S) * TILE, (t + 1) * TS, c, 1, wave_u);
+        dma_issue<NW, TS>(kdma, kblk, smem + (1 - S) * TILE, (t + 1) * TS, c, a.row_step, wave_u);
+        dma_issue<NW, TS>(vdma, vblk, smem + (3 - S) * TILE, (t + 1) * TS, c, a.row_step, wave_u);
       }
       const int cls = tile_class(t);
       if (cls) compute(smem + S * TILE, smem + (2 + S) * TILE, t, cls == 2);
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(RA_BWD_DQ_NW * 64, 2) void k_bwd_dq_bf16(BwdArgs a)
   }
 
   if (y < c)
-    store_rows(a.dq + bh * a.dq_bh_stride + ((int64_t)dev * c + y) * D, acc, a.scale, hh, a.accumulate != 0);
+    store_rows(a.dq + bh * a.dq_bh_stride + dev * a.dq_dev_stride + y * rstride, acc, a.scale, hh, a.accumulate != 0);
 }
 
 // ---------------------------------------------------------------------------- dK/dV kernel
@@ -282,10 +283,11 @@ __global__ __launch_bounds__(RA_BWD_DKV_NW * 64, 2) void k_bwd_dkv_bf16(BwdArgs 
   const int rw0 = a_rowwise_off<SWZ_T>(lane, 0);
   const int tr0 = a_tr_off<SWZ_T>(lane, 0, 0);
   unsigned dma[DmaShape<NW, TS>::PER_WAVE];
-  dma_init<NW, TS>(dma, SWZ_T, wave_u, lane, 1);
+  dma_init<NW, TS>(dma, SWZ_T, wave_u, lane, a.row_step);
 
   // B operands: this lane's key row of K and V
-  const int64_t kvo = bh * a.kv_bh_stride + (int64_t)kvi * a.kv_blk_stride + (int64_t)x * D + hh * 8;
+  const int64_t rstride = (int64_t)a.row_step * D;   // elements between rows of a block
+  const int64_t kvo = bh * a.kv_bh_stride + (int64_t)kvi * a.kv_blk_stride + x * rstride + hh * 8;
   bf16x8 kf[8], vf[8];
 #pragma unroll
   for (int dk = 0; dk < 8; ++dk) {
@@ -315,17 +317,20 @@ __global__ __launch_bounds__(RA_BWD_DKV_NW * 64, 2) void k_bwd_dkv_bf16(BwdArgs 
 
     auto issue = [&](int t, int S) __attribute__((always_inline)) {
       const int y0 = t * TS;
-      dma_issue<NW, TS>(dma, qblk, smem + S * TILE, y0, c, 1, wave_u);
-      dma_issue<NW, TS>(dma, oblk, smem + (2 + S) * TILE, y0, c, 1, wave_u);
+      dma_issue<NW, TS>(dma, qblk, smem + S * TILE, y0, c, a.row_step, wave_u);
+      dma_issue<NW, TS>(dma, oblk, smem + (2 + S) * TILE, y0, c, a.row_step, wave_u);
       if (wave_u == 0 && lane < 32) {
         // lane i < 32 copies L and D of row y0 + i to bytes 4 i of the stage's L and D areas;
-        // rows past the block end read as 0
+        // the descriptors end after the block's last row, so rows past it read as 0
         char* rs = smem + 4 * TILE + S * RS_BYTES;
-        const unsigned bytes = (unsigned)(c - y0) * 4;
-        const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc((void*)(lblk + y0), 0, bytes, 0x00020000);
-        const __amdgpu_buffer_rsrc_t dr = __builtin_amdgcn_make_buffer_rsrc((void*)(dblk + y0), 0, bytes, 0x00020000);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(lr, (lds_void*)rs, 4, (unsigned)(lane * 4), 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(dr, (lds_void*)(rs + TS * 4), 4, (unsigned)(lane * 4), 0, 0, 0);
+        const unsigned last = (unsigned)(min(c - y0, TS) - 1);
+        const int bytes = (int)((last * (unsigned)a.row_step + 1) * 4);
+        const int64_t base = (int64_t)y0 * a.row_step;
+        const unsigned off = (unsigned)lane * (unsigned)a.row_step * 4;
+        const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc((void*)(lblk + base), 0, bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t dr = __builtin_amdgcn_make_buffer_rsrc((void*)(dblk + base), 0, bytes, 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(lr, (lds_void*)rs, 4, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(dr, (lds_void*)(rs + TS * 4), 4, off, 0, 0, 0);
       }
     };
 
@@ -432,7 +437,7 @@ __global__ __launch_bounds__(RA_BWD_DKV_NW * 64, 2) void k_bwd_dkv_bf16(BwdArgs 
   }
 
   if (x < c) {
-    const int64_t ro = bh * a.dkv_bh_stride + ((int64_t)kvi * c + x) * D;
+    const int64_t ro = bh * a.dkv_bh_stride + (int64_t)kvi * a.dkv_blk_stride + x * rstride;
     store_rows(a.dk + ro, dka, a.scale, hh, a.accumulate != 0);
     store_rows(a.dv + ro, dva, 1.0f, hh, a.accumulate != 0);
   }

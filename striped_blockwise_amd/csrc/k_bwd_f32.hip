@@ -37,14 +37,15 @@ __global__ __launch_bounds__(64) void k_bwd_dq_f32(BwdArgs a) {
   const int q_last = min(c, q0 + TR) - 1;
 
   const float cs = a.scale * LOG2E;
+  const int64_t rstride = (int64_t)a.row_step * D;        // elements between rows of a block
   float qv[D], dov[D], dq[D];
   float nl = 0.f, dl = 0.f;
   if (y < c) {
-    const float* qp = (const float*)a.q + bh * a.q_bh_stride + dev * a.q_dev_stride + (int64_t)y * D;
-    const float* dop = (const float*)a.dout + bh * a.do_bh_stride + dev * a.do_dev_stride + (int64_t)y * D;
+    const float* qp = (const float*)a.q + bh * a.q_bh_stride + dev * a.q_dev_stride + y * rstride;
+    const float* dop = (const float*)a.dout + bh * a.do_bh_stride + dev * a.do_dev_stride + y * rstride;
 #pragma unroll
     for (int j = 0; j < D; ++j) { qv[j] = qp[j] * cs; dov[j] = dop[j]; }
-    const int64_t ro = bh * a.row_bh_stride + dev * a.row_dev_stride + y;
+    const int64_t ro = bh * a.row_bh_stride + dev * a.row_dev_stride + (int64_t)y * a.row_step;
     nl = -fmaxf(a.lse[ro], NEG_BIG) * LOG2E;
     dl = a.delta[ro];
   } else {
@@ -71,8 +72,8 @@ __global__ __launch_bounds__(64) void k_bwd_dq_f32(BwdArgs a) {
       __syncthreads();
       for (int i = lane; i < TS * D; i += 64) {
         const int row = x0 + i / D;
-        sk[i] = row < c ? kp[(int64_t)row * D + i % D] : 0.f;
-        sv[i] = row < c ? vp[(int64_t)row * D + i % D] : 0.f;
+        sk[i] = row < c ? kp[row * rstride + i % D] : 0.f;
+        sv[i] = row < c ? vp[row * rstride + i % D] : 0.f;
       }
       __syncthreads();
       for (int j = 0; j < TS; ++j) {
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(64) void k_bwd_dq_f32(BwdArgs a) {
     }
   }
   if (y < c) {
-    float* out = a.dq + bh * a.dq_bh_stride + ((int64_t)dev * c + y) * D;
+    float* out = a.dq + bh * a.dq_bh_stride + dev * a.dq_dev_stride + y * rstride;
 #pragma unroll
     for (int e = 0; e < D; ++e) out[e] = dq[e] * a.scale + (a.accumulate ? out[e] : 0.f);
   }
@@ -117,7 +118,8 @@ __global__ __launch_bounds__(64) void k_bwd_dkv_f32(BwdArgs a) {
 
   const float cs = a.scale * LOG2E;
   float kv[D], vv[D], dk[D], dv[D];
-  const int64_t kvo = bh * a.kv_bh_stride + (int64_t)kvi * a.kv_blk_stride + (int64_t)x * D;
+  const int64_t rstride = (int64_t)a.row_step * D;        // elements between rows of a block
+  const int64_t kvo = bh * a.kv_bh_stride + (int64_t)kvi * a.kv_blk_stride + x * rstride;
 #pragma unroll
   for (int j = 0; j < D; ++j) {
     kv[j] = x < c ? ((const float*)a.k)[kvo + j] * cs : 0.f;
@@ -142,13 +144,13 @@ __global__ __launch_bounds__(64) void k_bwd_dkv_f32(BwdArgs a) {
       __syncthreads();
       for (int i = lane; i < TS * D; i += 64) {
         const int row = y0 + i / D;
-        sq[i] = row < c ? qp[(int64_t)row * D + i % D] : 0.f;
-        so[i] = row < c ? dop[(int64_t)row * D + i % D] : 0.f;
+        sq[i] = row < c ? qp[row * rstride + i % D] : 0.f;
+        so[i] = row < c ? dop[row * rstride + i % D] : 0.f;
       }
       {
         const int row = y0 + lane;
-        sl[lane] = row < c ? -fmaxf(lp[row], NEG_BIG) * LOG2E : 0.f;
-        sd[lane] = row < c ? dp_[row] : 0.f;
+        sl[lane] = row < c ? -fmaxf(lp[(int64_t)row * a.row_step], NEG_BIG) * LOG2E : 0.f;
+        sd[lane] = row < c ? dp_[(int64_t)row * a.row_step] : 0.f;
       }
       __syncthreads();
       for (int j = 0; j < TS; ++j) {
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(64) void k_bwd_dkv_f32(BwdArgs a) {
     }
   }
   if (x < c) {
-    const int64_t ro = bh * a.dkv_bh_stride + ((int64_t)kvi * c + x) * D;
+    const int64_t ro = bh * a.dkv_bh_stride + (int64_t)kvi * a.dkv_blk_stride + x * rstride;
 #pragma unroll
     for (int e = 0; e < D; ++e) {
       a.dk[ro + e] = dk[e] * a.scale + (a.accumulate ? a.dk[ro + e] : 0.f);

@@ -358,8 +358,9 @@ ra_status_t ra_backward_round(const ra_problem_t* prob, const void* q, const voi
   a.q = q; a.dout = dout; a.lse = lse; a.delta = delta; a.k = k; a.v = v;
   a.q_bh_stride = q_stride_bh; a.do_bh_stride = do_stride_bh;
   a.row_bh_stride = row_stride_bh; a.kv_bh_stride = kv_stride_bh;
-  a.dq = dq_acc; a.dq_bh_stride = c * d;
-  a.dk = dk_acc; a.dv = dv_acc; a.dkv_bh_stride = c * d;
+  a.row_step = 1;
+  a.dq = dq_acc; a.dq_bh_stride = c * d; a.dq_dev_stride = c * d;
+  a.dk = dk_acc; a.dv = dv_acc; a.dkv_bh_stride = c * d; a.dkv_blk_stride = c * d;
   a.c = (int)c; a.P = prob->P; a.BH = (int)BH;
   a.p_begin = p; a.n_dev = 1;
   a.kv_base = kv; a.n_kv = 1;
@@ -375,8 +376,6 @@ ra_status_t ra_backward(const ra_problem_t* prob, const void* q, const void* k, 
                         int32_t p_end, float* dq, float* dk, float* dv, void* stream) {
   ra_status_t st = check_problem(prob);
   if (st != RA_OK) return st;
-  st = check_block_layout(prob);
-  if (st != RA_OK) return st;
   st = check_bwd_support(prob);
   if (st != RA_OK) return st;
   if (p_begin < 0 || p_end > prob->P || p_begin >= p_end)
@@ -391,21 +390,36 @@ ra_status_t ra_backward(const ra_problem_t* prob, const void* q, const void* k, 
   const int64_t d = prob->d;
   const int64_t BH = prob->B * prob->H;
   const int64_t ndev = p_end - p_begin;
-  const int64_t m = ndev * c;
+  const bool tokens = prob->layout == RA_STRIPED_TOKENS;
+  const int64_t m = tokens ? prob->n : ndev * c;     // rows of dout, lse, delta and dq
   st = check_grad_outputs(dq, BH * m * d * 4, dk, dv, BH * prob->n * d * 4);
   if (st != RA_OK) return st;
+  const int64_t eb = elem_bytes(prob->dtype);
   ra::BwdArgs a{};
-  a.q = (const char*)q + (int64_t)p_begin * c * d * elem_bytes(prob->dtype);
-  a.dout = dout; a.lse = lse; a.delta = delta; a.k = k; a.v = v;
+  a.k = k; a.v = v;
   a.q_bh_stride = prob->n * d; a.do_bh_stride = m * d; a.row_bh_stride = m; a.kv_bh_stride = prob->n * d;
-  a.q_dev_stride = c * d; a.do_dev_stride = c * d; a.row_dev_stride = c; a.kv_blk_stride = c * d;
-  a.dq = dq; a.dq_bh_stride = m * d;
+  a.dq_bh_stride = m * d;
   a.dk = dk; a.dv = dv; a.dkv_bh_stride = prob->n * d;
+  if (tokens) {
+    // Row y of device p's block is token y * P + p of the token-order tensors.
+    const int64_t r0 = p_begin;
+    a.q = (const char*)q + r0 * d * eb; a.dout = (const char*)dout + r0 * d * eb;
+    a.lse = lse + r0; a.delta = delta + r0; a.dq = dq + r0 * d;
+    a.q_dev_stride = d; a.do_dev_stride = d; a.row_dev_stride = 1; a.dq_dev_stride = d;
+    a.kv_blk_stride = d; a.dkv_blk_stride = d;
+    a.row_step = prob->P;
+  } else {
+    a.q = (const char*)q + (int64_t)p_begin * c * d * eb;
+    a.dout = dout; a.lse = lse; a.delta = delta; a.dq = dq;
+    a.q_dev_stride = c * d; a.do_dev_stride = c * d; a.row_dev_stride = c; a.dq_dev_stride = c * d;
+    a.kv_blk_stride = c * d; a.dkv_blk_stride = c * d;
+    a.row_step = 1;
+  }
   a.c = (int)c; a.P = prob->P; a.BH = (int)BH;
   a.p_begin = p_begin; a.n_dev = (int)ndev;
   a.kv_base = 0; a.n_kv = prob->P;
   a.r_begin = 0; a.r_count = prob->P;
-  a.layout = prob->layout; a.causal = prob->causal;
+  a.layout = tokens ? RA_STRIPED : prob->layout; a.causal = prob->causal;
   a.scale = eff_scale(prob);
   a.accumulate = 0;
   return launch_bwd(prob, a, (hipStream_t)stream);

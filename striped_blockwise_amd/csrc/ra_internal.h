@@ -83,11 +83,16 @@ struct BwdArgs {
   int64_t do_dev_stride;  // ... of dout
   int64_t row_dev_stride; // ... of lse and delta
   int64_t kv_blk_stride;  // elements between K/V blocks
-  float* dq;              // rows of device p_begin, then p_begin+1, ...: [(b,h)][n_dev*c][d]
+  int row_step;           // rows between consecutive rows of a block in every row-indexed
+                          // tensor (q, dout, lse, delta, k, v, dq, dk, dv): 1, or P for a
+                          // striped block of a token-order tensor
+  float* dq;              // rows of device p_begin, then p_begin+1, ...
   int64_t dq_bh_stride;
-  float* dk;              // rows of block kv_base, then kv_base+1, ...: [(b,h)][n_kv*c][d]
+  int64_t dq_dev_stride;  // elements between the first rows of consecutive devices in dq
+  float* dk;              // rows of block kv_base, then kv_base+1, ...
   float* dv;
   int64_t dkv_bh_stride;
+  int64_t dkv_blk_stride; // elements between the first rows of consecutive blocks in dk, dv
   int c;                  // rows per block
   int P;                  // devices
   int BH;                 // B * H

@@ -133,8 +133,8 @@ def test_backward_host_validation(ra):
 
 
 def test_token_order_layout_host_validation(ra):
-    """RA_STRIPED_TOKENS is accepted by ra_forward's validation and refused (unsupported, nothing
-    launched) by the per-round and backward entry points."""
+    """RA_STRIPED_TOKENS is accepted by ra_forward's and ra_backward's validation and refused
+    (unsupported, nothing launched) by the per-round entry points."""
     L = ra.lib()
     N = None
     pr = ra._problem(1, 1, 256, 128, 4, ra.BF16, ra.STRIPED_TOKENS, True, 0.0)
@@ -143,7 +143,8 @@ def test_token_order_layout_host_validation(ra):
     assert b"NULL" in L.ra_last_error()
     assert L.ra_round(ctypes.byref(pr), N, N, N, 0, 0, 0, 0, N, N, N, N) == -2
     assert b"layout order" in L.ra_last_error()
-    assert L.ra_backward(ctypes.byref(pr), *(N,) * 6, 0, 4, N, N, N, N) == -2
+    assert L.ra_backward(ctypes.byref(pr), *(N,) * 6, 0, 4, N, N, N, N) == -1        # NULL, not layout
+    assert b"NULL" in L.ra_last_error()
     assert L.ra_backward_round(ctypes.byref(pr), *(N,) * 6, 0, 0, 0, 0, 1, 0, N, N, N, N) == -2
 
 

@@ -1,4 +1,4 @@
-"""GPU parity of the token-order striped layout (RA_STRIPED_TOKENS) of ra_forward.
+"""GPU parity of the token-order striped layout (RA_STRIPED_TOKENS) of ra_forward and ra_backward.
 
 The partition, ring schedule and GetMask are those of the striped layout (Striped Attention
 review, "分区策略对比" and "GetMask 函数"); only the addressing differs: the kernels read and write
@@ -9,7 +9,9 @@ Checked here:
 * bit-exact against the permuted path (ra_permute, ra_forward on RA_STRIPED, inverse ra_permute
   of O and LSE): both run the same arithmetic in the same order on the same values;
 * the work counters equal the striped layout's closed forms;
-* a device range writes only its own rows (token t with p_begin <= t mod P < p_end).
+* a device range writes only its own rows (token t with p_begin <= t mod P < p_end);
+* the backward: gradients against the oracle's fp64 autograd in token order, and bit-exact
+  against the permuted path (permute, backward on RA_STRIPED, inverse permute of dQ, dK, dV).
 """
 from __future__ import annotations
 
@@ -19,8 +21,9 @@ import torch
 
 import workloads
 from oracle import attention as OA
+from oracle import backward as OB
 from oracle import ring as OR
-from tests._gpu_util import compare, need_gpu, np64
+from tests._gpu_util import compare, compare_grad, need_gpu, np64
 
 pytestmark = pytest.mark.gpu
 
@@ -129,3 +132,58 @@ def test_token_order_rejected_where_unsupported(ra):
     o = torch.empty((1, 1, 128, 128), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ValueError, match="out\\[0\\]"):                     # o must hold all n rows
         ra.forward(x, x, x, 4, "striped_tokens", True, p_begin=0, p_end=2, out=(o, None))
+
+
+# --------------------------------------------------------------------------- backward
+def _grads_via_permutes(ra, q, k, v, g, P, causal):
+    """The permuted path: ra_permute, forward and backward on RA_STRIPED, gradients back to token
+    order with the inverse permutation."""
+    qs, ks, vs, gs = (ra.permute(t, P) for t in (q, k, v, g))
+    o, lse = ra.forward(qs, ks, vs, P, "striped", causal)
+    dq, dk, dv = ra.backward(qs, ks, vs, gs, lse, P, "striped", causal, o=o)
+    return tuple(ra.permute(t, P, inverse=True) for t in (dq, dk, dv))
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64)])
+@pytest.mark.parametrize("P,c", [(4, 37), (8, 200), (3, 512), (1, 96), (64, 2)])
+def test_token_order_backward_matches_oracle(ra, dtype, d, P, c):
+    B, H = 1, 2
+    n = P * c
+    gen = torch.Generator().manual_seed(3000 + 11 * c + P + d)
+    q, k, v, g = (torch.randn((B, H, n, d), generator=gen).mul(0.5 if i < 3 else 1.0).to(dtype) for i in range(4))
+    ref = OB.attention_grads(q, k, v, g, True)                   # token order, positions 0..n-1
+    kind = "f32" if dtype == torch.float32 else "bf16"
+    qg, kg, vg, gg = (t.cuda() for t in (q, k, v, g))
+    o, lse = ra.forward(qg, kg, vg, P, "striped_tokens", True)
+    got = ra.backward(qg, kg, vg, gg, lse, P, "striped_tokens", True, o=o)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        compare_grad(a, b, kind, f"token order P={P} c={c} {name}")
+    via = _grads_via_permutes(ra, qg, kg, vg, gg, P, True)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), got, via):
+        assert torch.equal(a, b), f"token-order {name} differs from the permuted path"
+
+
+def test_token_order_backward_device_range(ra):
+    """Devices 1..2 of 4: dq only on their rows (others untouched), dk and dv everywhere, equal to
+    the oracle's gradient of those queries' loss."""
+    P, c, H, d = 4, 130, 2, 128
+    n = P * c
+    gen = torch.Generator().manual_seed(41)
+    q, k, v, g = (torch.randn((1, H, n, d), generator=gen).to(torch.bfloat16) for _ in range(4))
+    mine = np.isin(np.arange(n) % P, [1, 2])
+    sel = torch.from_numpy(np.nonzero(mine)[0])
+    ref = OB.attention_grads(q[:, :, sel], k, v, g[:, :, sel], True, pos_q=sel.numpy(), pos_k=np.arange(n))
+    qg, kg, vg, gg = (t.cuda() for t in (q, k, v, g))
+    o, lse = ra.forward(qg, kg, vg, P, "striped_tokens", True, p_begin=1, p_end=3)
+    dq = torch.full((1, H, n, d), float("nan"), device="cuda")
+    dk = torch.empty((1, H, n, d), device="cuda")
+    dv = torch.empty((1, H, n, d), device="cuda")
+    ra.backward(qg, kg, vg, gg, lse, P, "striped_tokens", True, 1, 3, o=o, out=(dq, dk, dv))
+    torch.cuda.synchronize()
+    dqn = np64(dq)
+    assert np.isnan(dqn[:, :, ~mine]).all(), "dq rows of other devices written"
+    compare_grad(dqn[:, :, mine], ref[0], "bf16", "range dq")
+    compare_grad(dk, ref[1], "bf16", "range dk")
+    compare_grad(dv, ref[2], "bf16", "range dv")
