@@ -1,6 +1,7 @@
 // bf16 blockwise attention on gfx950 matrix cores (v_mfma_f32_32x32x16_bf16), head dim 128.
 //
-// What one workgroup computes: NW wavefronts x QW query rows of device p's Q block, against
+// What one workgroup computes: NW wavefronts x QW query rows of device p's Q block (NW = 12,
+// or 4 when the grid would not give every CU two workgroups), against
 // the K/V blocks of the ring rounds it is given (Ring Attention review, step 2: round r brings
 // the block of device (p - r) mod P), folding each round in with the online softmax (step 3).
 // Masks follow the GetMask procedures of the Striped Attention review ("GetMask 函数"), applied
@@ -9,8 +10,10 @@
 //
 // Data flow per TK-key tile:
 //   HBM -> LDS by DMA (buffer_load ... lds, 16 B per lane), K and V both row-major with a
-//   per-row XOR swizzle of their 16-byte chunks; no registers or VALU work on the way in.  Two
-//   LDS stages: the next tile's load is in flight while this tile computes.
+//   per-row XOR swizzle of their 16-byte chunks; no registers or VALU work on the way in.  A
+//   block's rows are consecutive in HBM, or P rows apart when a striped block is read straight
+//   from a token-order tensor (row y of block k is token y P + k).  Two LDS stages: the next
+//   tile's load is in flight while this tile computes.
 //   S^T = K Q^T on MFMA: A = 32 K rows from LDS, B = the wavefront's Q columns in registers.
 //   In this orientation each lane owns one query, so the row max / row sum are in-lane
 //   reductions plus one v_permlane32_swap with the other half of the wavefront.

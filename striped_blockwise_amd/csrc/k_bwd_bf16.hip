@@ -22,6 +22,8 @@
 //                 dS = P * (dP - D) in registers (one key per lane),
 //                 dV^T += dO^T P, dK^T += Q^T dS (A = dO / Q read transposed).
 // A tile read both row-wise and transposed uses the t_swz chunk mask, conflict-free for both.
+// Every row-indexed tensor is addressed with the same row step: consecutive rows of a block, or
+// rows P apart for a striped block of a token-order tensor (row y of block k is token y P + k).
 // Rows past the end of a block arrive in LDS as zeros: a zero query row with L = D = 0 gives
 // P = 1 and dS = 0 and adds nothing; zero key rows are masked in the dQ kernel and only reach
 // their own (unwritten) dK/dV columns in the dK/dV kernel.
