@@ -187,3 +187,26 @@ def test_token_order_backward_device_range(ra):
     compare_grad(dqn[:, :, mine], ref[0], "bf16", "range dq")
     compare_grad(dk, ref[1], "bf16", "range dk")
     compare_grad(dv, ref[2], "bf16", "range dv")
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "striped_tokens"])
+def test_batch_of_two_forward_and_backward(ra, layout):
+    """B = 2, H = 3: the kernels flatten (b, h) into one stride; every (b, h) matrix must match."""
+    B, H, P, c, d = 2, 3, 4, 70, 128
+    n = P * c
+    gen = torch.Generator().manual_seed(555)
+    q, k, v, g = (torch.randn((B, H, n, d), generator=gen).mul(0.5 if i < 3 else 1.0).to(torch.bfloat16)
+                  for i in range(4))
+    o_ref, l_ref = OA.attention(q, k, v, True)
+    dq_ref, dk_ref, dv_ref = OB.attention_grads(q, k, v, g, True)
+    order = OR.layout_order(n, P, "striped" if layout == "striped" else "contiguous")
+    idx = torch.from_numpy(order)
+    to_l = (lambda t: t[:, :, idx].contiguous()) if layout == "striped" else (lambda t: t)
+    qg, kg, vg, gg = (to_l(t).cuda() for t in (q, k, v, g))
+    o, lse = ra.forward(qg, kg, vg, P, layout, True, o_dtype=torch.float32)
+    dq, dk, dv = ra.backward(qg, kg, vg, gg, lse, P, layout, True, o=o)
+    torch.cuda.synchronize()
+    back = (lambda t: t[:, :, torch.from_numpy(np.argsort(order))]) if layout == "striped" else (lambda t: t)
+    compare(back(o.cpu()), back(lse.cpu()), o_ref, l_ref, "bf16", f"B=2 {layout}")
+    for name, got, ref in (("dq", dq, dq_ref), ("dk", dk, dk_ref), ("dv", dv, dv_ref)):
+        compare_grad(back(got.cpu()), ref, "bf16", f"B=2 {layout} {name}")
