@@ -1,17 +1,36 @@
-// Row-movement and row-combination kernels: the striped permutation and the log-sum-exp merge.
-// Both are HBM-bandwidth bound; each lane moves 16 bytes per access where the row allows it.
+// Row-movement and row-combination kernels: the striped permutation (plain, and fused with the
+// rotary embedding), the log-sum-exp merge and the backward's row term D.  All are
+// HBM-bandwidth bound; each lane moves 16 bytes per access where the row allows it.
 #include "ra_internal.h"
 
 namespace ra {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+#ifndef RA_ROWS_NT
+#define RA_ROWS_NT 1            // 1: streamed loads and stores marked non-temporal (merge, delta, RoPE)
+#endif
+// Every byte these kernels move is touched once, so marking the accesses non-temporal keeps
+// them from displacing useful lines in the caches.
+template <typename V>
+__device__ __forceinline__ V ld_stream(const V* p) {
+  if (RA_ROWS_NT) return __builtin_nontemporal_load(p);
+  return *p;
+}
+template <typename V>
+__device__ __forceinline__ void st_stream(V v, V* p) {
+  if (RA_ROWS_NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
 
 // ---------------------------------------------------------------------------------------------
 // Striped permutation (Striped Attention review, "分区策略对比" / "位置编码处理"): token t goes
 // to device t mod P, slot t / P, i.e. layout row pi(t) = (t mod P) * c + t / P.  Grid-stride
 // over destination chunks so that writes are sequential; the rows being read are the
-// scattered side.  VEC is the bytes one lane moves (16 or 4).
+// scattered side.  VEC is the bytes one lane moves (16 or 4).  This general form serves rows
+// that k_permute_rows below does not take (LSE values, position IDs, odd row sizes).
 template <int VEC>
 __global__ __launch_bounds__(256) void k_permute(const char* __restrict__ src,
                                                  char* __restrict__ dst, uint64_t total,
@@ -36,6 +55,56 @@ __global__ __launch_bounds__(256) void k_permute(const char* __restrict__ src,
     const T* s = reinterpret_cast<const T*>(src + (bh * n + srow) * row_bytes) + ch;
     T* d = reinterpret_cast<T*>(dst + row_lin * row_bytes) + ch;
     *d = *s;
+  }
+}
+
+#ifndef RA_PERMUTE_IMPL
+#define RA_PERMUTE_IMPL 2       // 0: element grid-stride kernel; 1: row kernel; 2: row kernel, non-temporal
+#endif
+
+// The same permutation, row by row, for rows of 16-byte chunks whose count divides 256: `lpr`
+// lanes move one row, a block pass covers 256 / lpr rows, and each thread keeps RPT rows in
+// flight.  One 32-bit division per row replaces the per-chunk 64-bit index arithmetic of
+// k_permute.  blockIdx.y is the (b, h) matrix (looping when BH exceeds the grid's y range).
+template <bool NTEMP>
+__global__ __launch_bounds__(256) void k_permute_rows(const char* __restrict__ src, char* __restrict__ dst,
+                                                      uint64_t BH, uint32_t n, uint32_t lpr, uint32_t P,
+                                                      uint32_t c, int inverse, uint64_t row_bytes) {
+  constexpr int RPT = 4;
+  const uint32_t rpp = 256 / lpr;                         // rows per block pass
+  const uint32_t r_in = threadIdx.x / lpr;
+  const uint32_t ch = threadIdx.x - r_in * lpr;
+  const uint32_t rows_per_block = rpp * RPT;
+  for (uint64_t bh = blockIdx.y; bh < BH; bh += gridDim.y) {
+    const char* sbase = src + bh * n * row_bytes;
+    char* dbase = dst + bh * n * row_bytes;
+    for (uint32_t r0 = blockIdx.x * rows_per_block; r0 < n; r0 += gridDim.x * rows_per_block) {
+      u32x4 v[RPT];
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) {
+        const uint32_t drow = r0 + k * rpp + r_in;
+        if (drow < n) {
+          uint32_t srow;
+          if (inverse) {
+            srow = (drow % P) * c + drow / P;             // dst[t] = src[pi(t)]
+          } else {
+            const uint32_t dev = drow / c;                // dst[pi(t)] = src[t]
+            srow = (drow - dev * c) * P + dev;
+          }
+          const u32x4* sp = reinterpret_cast<const u32x4*>(sbase + (uint64_t)srow * row_bytes) + ch;
+          v[k] = NTEMP ? __builtin_nontemporal_load(sp) : *sp;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) {
+        const uint32_t drow = r0 + k * rpp + r_in;
+        if (drow < n) {
+          u32x4* dp = reinterpret_cast<u32x4*>(dbase + (uint64_t)drow * row_bytes) + ch;
+          if (NTEMP) __builtin_nontemporal_store(v[k], dp);
+          else *dp = v[k];
+        }
+      }
+    }
   }
 }
 
@@ -75,13 +144,11 @@ __global__ __launch_bounds__(256) void k_merge(float* __restrict__ o_acc, float*
     const float* ob = o_part + row * d;
     if (vec4) {
       for (int64_t j = li; j < (d >> 2); j += LPR) {
-        float4 a = reinterpret_cast<float4*>(oa)[j];
-        const float4 b = reinterpret_cast<const float4*>(ob)[j];
-        a.x = wa * a.x + wb * b.x;
-        a.y = wa * a.y + wb * b.y;
-        a.z = wa * a.z + wb * b.z;
-        a.w = wa * a.w + wb * b.w;
-        reinterpret_cast<float4*>(oa)[j] = a;
+        f32x4v a = ld_stream(reinterpret_cast<const f32x4v*>(oa) + j);
+        const f32x4v b = ld_stream(reinterpret_cast<const f32x4v*>(ob) + j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = wa * a[e] + wb * b[e];
+        st_stream(a, reinterpret_cast<f32x4v*>(oa) + j);
       }
     } else {
       for (int64_t j = li; j < d; j += LPR) oa[j] = wa * oa[j] + wb * ob[j];
@@ -93,10 +160,13 @@ __global__ __launch_bounds__(256) void k_merge(float* __restrict__ o_acc, float*
 // ---------------------------------------------------------------------------------------------
 // Backward row term D_i = sum_e O_ie dO_ie (fp32 sums).  16 lanes of one wavefront per row, each
 // taking groups of 4 consecutive elements (or single elements when d % 4 != 0).
-__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4(const float* p) {
+  const f32x4v v = ld_stream(reinterpret_cast<const f32x4v*>(p));
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
 __device__ __forceinline__ float4 load4(const __bf16* p) {
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  const bf16x4 v = ld_stream(reinterpret_cast<const bf16x4*>(p));
   return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
 }
 
@@ -196,7 +266,7 @@ template <> struct Vec<4, float> { typedef float type __attribute__((ext_vector_
 
 template <int N, typename T>
 __device__ __forceinline__ void load_n(const T* p, double (&v)[N]) {
-  const typename Vec<N, T>::type x = *reinterpret_cast<const typename Vec<N, T>::type*>(p);
+  const typename Vec<N, T>::type x = ld_stream(reinterpret_cast<const typename Vec<N, T>::type*>(p));
 #pragma unroll
   for (int i = 0; i < N; ++i) v[i] = (double)(float)x[i];
 }
@@ -205,7 +275,7 @@ __device__ __forceinline__ void store_n(T* p, const double (&v)[N]) {
   typename Vec<N, T>::type x;
 #pragma unroll
   for (int i = 0; i < N; ++i) x[i] = (T)(float)v[i];
-  *reinterpret_cast<typename Vec<N, T>::type*>(p) = x;
+  st_stream(x, reinterpret_cast<typename Vec<N, T>::type*>(p));
 }
 
 template <typename T, bool HALF>
@@ -220,6 +290,9 @@ __global__ __launch_bounds__(256) void k_rope_permute_vec(const T* __restrict__ 
   const uint32_t rows_per_step = 64 / units;
   const uint32_t u = lane % units;
   const uint32_t rsub = lane / units;
+  double theta[4];                                  // this lane's pairs 4u .. 4u+3
+#pragma unroll
+  for (int j = 0; j < 4; ++j) theta[j] = pow(base, -2.0 * (double)(4 * u + j) / (double)d);
   for (uint64_t tt = wave; tt < n; tt += nwaves) {
     const uint32_t t = (uint32_t)tt;
     const uint32_t lrow = striped ? (t % P) * c + t / P : t;
@@ -229,33 +302,59 @@ __global__ __launch_bounds__(256) void k_rope_permute_vec(const T* __restrict__ 
     double cs[4], sn[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const double theta = pow(base, -2.0 * (double)(4 * u + j) / (double)d);
-      sincos(m * theta, &sn[j], &cs[j]);
+      sincos(m * theta[j], &sn[j], &cs[j]);
       if (inverse) sn[j] = -sn[j];
     }
-    for (int64_t bh = rsub; bh < BH; bh += rows_per_step) {
-      const T* srow_p = src + ((uint64_t)bh * n + srow) * d;
-      T* drow_p = dst + ((uint64_t)bh * n + drow) * d;
+    // two (b, h) rows per step, both loaded before either is rotated
+    for (int64_t bh0 = rsub; bh0 < BH; bh0 += 2 * (int64_t)rows_per_step) {
+      const bool two = bh0 + rows_per_step < BH;
+      const int64_t bh1 = two ? bh0 + rows_per_step : bh0;
+      const T* s0 = src + ((uint64_t)bh0 * n + srow) * d;
+      const T* s1 = src + ((uint64_t)bh1 * n + srow) * d;
+      T* d0 = dst + ((uint64_t)bh0 * n + drow) * d;
+      T* d1 = dst + ((uint64_t)bh1 * n + drow) * d;
       if (HALF) {
-        double a[4], b[4], oa[4], ob[4];
-        load_n<4>(srow_p + 4 * u, a);
-        load_n<4>(srow_p + d / 2 + 4 * u, b);
+        double a0[4], b0[4], a1[4], b1[4], oa[4], ob[4];
+        load_n<4>(s0 + 4 * u, a0);
+        load_n<4>(s0 + d / 2 + 4 * u, b0);
+        if (two) {
+          load_n<4>(s1 + 4 * u, a1);
+          load_n<4>(s1 + d / 2 + 4 * u, b1);
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          oa[j] = fma(a[j], cs[j], -b[j] * sn[j]);
-          ob[j] = fma(a[j], sn[j], b[j] * cs[j]);
+          oa[j] = fma(a0[j], cs[j], -b0[j] * sn[j]);
+          ob[j] = fma(a0[j], sn[j], b0[j] * cs[j]);
         }
-        store_n<4>(drow_p + 4 * u, oa);
-        store_n<4>(drow_p + d / 2 + 4 * u, ob);
+        store_n<4>(d0 + 4 * u, oa);
+        store_n<4>(d0 + d / 2 + 4 * u, ob);
+        if (two) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            oa[j] = fma(a1[j], cs[j], -b1[j] * sn[j]);
+            ob[j] = fma(a1[j], sn[j], b1[j] * cs[j]);
+          }
+          store_n<4>(d1 + 4 * u, oa);
+          store_n<4>(d1 + d / 2 + 4 * u, ob);
+        }
       } else {
-        double e[8], o[8];
-        load_n<8>(srow_p + 8 * u, e);
+        double e0[8], e1[8], o[8];
+        load_n<8>(s0 + 8 * u, e0);
+        if (two) load_n<8>(s1 + 8 * u, e1);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          o[2 * j] = fma(e[2 * j], cs[j], -e[2 * j + 1] * sn[j]);
-          o[2 * j + 1] = fma(e[2 * j], sn[j], e[2 * j + 1] * cs[j]);
+          o[2 * j] = fma(e0[2 * j], cs[j], -e0[2 * j + 1] * sn[j]);
+          o[2 * j + 1] = fma(e0[2 * j], sn[j], e0[2 * j + 1] * cs[j]);
         }
-        store_n<8>(drow_p + 8 * u, o);
+        store_n<8>(d0 + 8 * u, o);
+        if (two) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            o[2 * j] = fma(e1[2 * j], cs[j], -e1[2 * j + 1] * sn[j]);
+            o[2 * j + 1] = fma(e1[2 * j], sn[j], e1[2 * j + 1] * cs[j]);
+          }
+          store_n<8>(d1 + 8 * u, o);
+        }
       }
     }
   }
@@ -276,6 +375,18 @@ hipError_t launch_permute(const void* src, void* dst, int64_t BH, int64_t n, int
   const bool v16 = (row_bytes % 16 == 0) && ((uintptr_t)src % 16 == 0) && ((uintptr_t)dst % 16 == 0);
   const int vec = v16 ? 16 : 4;
   const uint32_t cpr = (uint32_t)(row_bytes / vec);
+  if (RA_PERMUTE_IMPL && v16 && cpr <= 256 && 256 % cpr == 0) {
+    const uint32_t rows_per_block = (256 / cpr) * 4;
+    const uint64_t gx = ((uint64_t)n + rows_per_block - 1) / rows_per_block;
+    const dim3 grid((unsigned)(gx < 1 ? 1 : gx), (unsigned)(BH < 65535 ? BH : 65535));
+    if (RA_PERMUTE_IMPL == 2)
+      hipLaunchKernelGGL(k_permute_rows<true>, grid, dim3(256), 0, s, (const char*)src, (char*)dst,
+                         (uint64_t)BH, (uint32_t)n, cpr, (uint32_t)P, c, inverse, (uint64_t)row_bytes);
+    else
+      hipLaunchKernelGGL(k_permute_rows<false>, grid, dim3(256), 0, s, (const char*)src, (char*)dst,
+                         (uint64_t)BH, (uint32_t)n, cpr, (uint32_t)P, c, inverse, (uint64_t)row_bytes);
+    return hipGetLastError();
+  }
   const uint64_t total = (uint64_t)BH * (uint64_t)n * cpr;
   const int grid = grid_for(total, 256 * 4);
   if (v16)
