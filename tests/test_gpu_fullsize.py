@@ -7,7 +7,8 @@
   contiguous one.
 * The backward of device 7's share (ra_backward), both layouts: dQ on sampled rows against the
   oracle, dK and dV through identities that hold at any size; the same share streamed round by
-  round through ra_backward_round equals the fused result; and the backward of the 1M stress
+  round through ra_backward_round equals the fused result; from token-order tensors it equals
+  the permuted path bit for bit; and the backward of the 1M stress
   share (device 31) under the same checks.
 * 1M-token stress (n = 1048576, P = 32, H = 8, 1% of K rows x8): device 31, striped, all 32
   rounds streamed through ra_round + ra_merge, and the same share fused with ra_forward.
@@ -243,6 +244,34 @@ def test_share256k_backward_rounds_equal_fused(ra, share):
     assert diff <= 1e-5 * float(dq.abs().max()), diff
     print(f"[fullsize] streamed backward vs fused: worst relative max diff {worst:.2e}", flush=True)
     del qs, ks, vs, dq, dk, dv, dq_r, dout, o, lse, delta
+    torch.cuda.empty_cache()
+
+
+def test_share256k_backward_token_order(ra, share):
+    """The backward of device 7's share from token-order tensors (RA_STRIPED_TOKENS): dQ on device
+    7's token rows and every dK/dV row equal, bit for bit, the permuted path's gradients mapped
+    back to token order."""
+    w, q, k, v = share
+    P, c, p = w.P, w.c, w.device
+    gen = torch.Generator(device="cuda").manual_seed(23)
+    dout_t = torch.randn((w.B, w.H, w.n, w.d), device="cuda", generator=gen).to(torch.bfloat16)
+    o_t, lse_t = ra.forward(q, k, v, P, "striped_tokens", True, p_begin=p, p_end=p + 1)
+    delta_t = ra.bwd_delta(o_t, dout_t)
+    dq_t, dk_t, dv_t = ra.backward(q, k, v, dout_t, lse_t, P, "striped_tokens", True, p, p + 1, delta=delta_t)
+    torch.cuda.synchronize()
+    del o_t
+    qs, ks, vs = (ra.permute(t, P) for t in (q, k, v))
+    dout_s = dout_t[:, :, p::P].contiguous()
+    o_s, lse_s = ra.forward(qs, ks, vs, P, "striped", True, p_begin=p, p_end=p + 1)
+    delta_s = ra.bwd_delta(o_s, dout_s)
+    dq_s, dk_s, dv_s = ra.backward(qs, ks, vs, dout_s, lse_s, P, "striped", True, p, p + 1, delta=delta_s)
+    del qs, ks, vs, o_s
+    torch.cuda.synchronize()
+    assert torch.equal(delta_t[:, :, p::P], delta_s), "delta"
+    assert torch.equal(dq_t[:, :, p::P], dq_s), "dq"
+    assert torch.equal(dk_t, ra.permute(dk_s, P, inverse=True)), "dk"
+    assert torch.equal(dv_t, ra.permute(dv_s, P, inverse=True)), "dv"
+    del dq_t, dk_t, dv_t, dq_s, dk_s, dv_s, dout_t, dout_s
     torch.cuda.empty_cache()
 
 
