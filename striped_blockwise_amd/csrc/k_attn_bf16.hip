@@ -26,6 +26,7 @@
 // because O, l and the reference max always stay consistent.  The tile max itself is only
 // computed when P against the current reference comes out large (a lane's partial row sum
 // above 2^12) or a row has no reference yet; otherwise that first P is kept.
+#include <atomic>
 #include <type_traits>
 
 #include "bf16_tile.h"
@@ -449,17 +450,18 @@ void attn_bf16_tile(int* tq, int* tk) { *tq = 32 * QB_SEL; *tk = TK_SEL; }
 
 namespace {
 
-// Compute units of the current device (queried once per device).
+// Compute units of the current device (queried once per device; concurrent first calls from
+// several host threads store the same value).
 int cu_count() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 template <int NW>
