@@ -236,3 +236,19 @@ def test_backward_invalid_args(ra):
         ra.backward(q48, q48, q48, q48, lse, 4, delta=lse)
     with pytest.raises(ValueError):
         ra.bwd_delta(q, q[:, :, :32])
+
+
+@pytest.mark.parametrize("c", [127, 129, 255, 257])
+def test_backward_workgroup_boundaries(ra, c):
+    """Block sizes around the backward kernels' workgroup tiles (128 key rows for dK/dV, 256 query
+    rows for dQ), both layouts, against the oracle."""
+    P, H, d = 2, 2, 128
+    n = P * c
+    gen = torch.Generator().manual_seed(9000 + c)
+    q, k, v, g = (torch.randn((1, H, n, d), generator=gen).mul(0.5 if i < 3 else 1.0).to(torch.bfloat16)
+                  for i in range(4))
+    for layout in LAYOUTS:
+        (ql, kl, vl, gl), order = _to_layout((q, k, v, g), P, layout)
+        got = _gpu_fwd_bwd(ra, ql, kl, vl, gl, P, layout, True)
+        ref = _oracle(ql, kl, vl, gl, P, order, True)
+        _check(got, ref, "bf16", f"c={c} {layout}")

@@ -410,3 +410,26 @@ def test_rising_scores_take_the_rescale_path(ra, H):
         torch.cuda.synchronize()
         idx = torch.tensor(heads, device="cuda")
         compare(o.index_select(1, idx), lse.index_select(1, idx), o_ref, l_ref, "bf16", f"rising H={H} {layout}")
+
+
+@pytest.mark.parametrize("H,c", [(256, 383), (256, 384), (256, 385), (2, 127), (2, 128), (2, 129)])
+def test_workgroup_tile_boundaries(ra, H, c):
+    """Block sizes at and around a workgroup's query tile: 384 rows for the 12-wave kernel (the
+    256-head cases, whose grids of at least two 12-wave workgroups per CU select it) and 128 rows
+    for the 4-wave kernel."""
+    B, P, d = 1, 2, 128
+    n = P * c
+    g = torch.Generator().manual_seed(7000 + c + H)
+    q, k, v = (torch.randn((B, H, n, d), generator=g).mul(0.5).to(torch.bfloat16) for _ in range(3))
+    heads = [0, H - 1]
+    for layout in ("contiguous", "striped"):
+        (ql, kl, vl), order = _oracle_layout(tuple(t[:, heads] for t in (q, k, v)), P, layout)
+        o_ref, l_ref = OA.attention(ql, kl, vl, True, pos_q=order, pos_k=order)
+        qg, kg, vg = (ra.permute(t.cuda(), P) if layout == "striped" else t.cuda() for t in (q, k, v))
+        stats = ra.new_stats(P)
+        o, lse = ra.forward(qg, kg, vg, P, layout, True, o_dtype=torch.float32, stats=stats)
+        torch.cuda.synchronize()
+        idx = torch.tensor(heads, device="cuda")
+        compare(o.index_select(1, idx), lse.index_select(1, idx), o_ref, l_ref, "bf16", f"c={c} H={H} {layout}")
+        tq, tk = ra.tile_shape(ra.BF16, d)
+        assert np.array_equal(stats.cpu().numpy(), _expected_stats(layout, P, c, B * H, True, tq, tk))
