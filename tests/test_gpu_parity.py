@@ -433,3 +433,29 @@ def test_workgroup_tile_boundaries(ra, H, c):
         compare(o.index_select(1, idx), lse.index_select(1, idx), o_ref, l_ref, "bf16", f"c={c} H={H} {layout}")
         tq, tk = ra.tile_shape(ra.BF16, d)
         assert np.array_equal(stats.cpu().numpy(), _expected_stats(layout, P, c, B * H, True, tq, tk))
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64)])
+@pytest.mark.parametrize("scale", [0.3, 1.0])
+def test_explicit_score_scale(ra, dtype, d, scale):
+    """A caller-given score scale replaces 1/sqrt(d), in the fused forward and in one round."""
+    P, c, H = 4, 96, 2
+    n = P * c
+    g = torch.Generator().manual_seed(int(scale * 100) + d)
+    q, k, v = (torch.randn((1, H, n, d), generator=g).mul(0.5).to(dtype) for _ in range(3))
+    kind = "f32" if dtype == torch.float32 else "bf16"
+    for layout in LAYOUTS:
+        (ql, kl, vl), order = _oracle_layout((q, k, v), P, layout)
+        o_ref, l_ref = OA.attention(ql, kl, vl, True, pos_q=order, pos_k=order, scale=scale)
+        qg, kg, vg = (ra.permute(t.cuda(), P) if layout == "striped" else t.cuda() for t in (q, k, v))
+        o, lse = ra.forward(qg, kg, vg, P, layout, True, o_dtype=torch.float32, scale=scale)
+        torch.cuda.synchronize()
+        compare(o, lse, o_ref, l_ref, kind, f"scale={scale} {layout}")
+        p, kk = 3, 1
+        po, pl = ra.round(qg[:, :, p * c:(p + 1) * c], kg[:, :, kk * c:(kk + 1) * c], vg[:, :, kk * c:(kk + 1) * c],
+                          P, p, kk, layout, True, scale=scale)
+        torch.cuda.synchronize()
+        for h in range(H):
+            ro, rl = OR.round_partial(ql[0, h, p * c:(p + 1) * c], kl[0, h, kk * c:(kk + 1) * c],
+                                      vl[0, h, kk * c:(kk + 1) * c], layout, p, kk, True, scale=scale)
+            compare(po[0, h], pl[0, h], ro, rl, kind, f"round scale={scale} {layout} h={h}")
