@@ -184,3 +184,42 @@ def test_product_package_never_touches_the_oracle():
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), f
                 assert "oracle/" not in text and "import workloads" not in text, f
+
+
+def test_header_is_plain_c_and_links(tmp_path, ra):
+    """include/ra.h compiles as C99, and a C program links against libra.so and runs the
+    host-only entry points (no GPU needed): the boundary is usable without C++ or Python."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "use_ra.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include <string.h>
+#include "ra.h"
+int main(void) {
+  ra_problem_t pr;
+  memset(&pr, 0, sizeof pr);
+  pr.B = 1; pr.H = 8; pr.n = 8192; pr.d = 128; pr.P = 4;
+  pr.dtype = RA_BF16; pr.layout = RA_STRIPED_TOKENS; pr.causal = 1; pr.scale = 0.0f;
+  if (ra_abi_version() != RA_ABI_VERSION) return 1;
+  if (ra_check(&pr, 3, 0) != RA_OK) return 2;
+  pr.n = 8190;                                   /* not a multiple of P */
+  if (ra_check(&pr, 0, 0) != RA_E_INVAL) return 3;
+  if (strstr(ra_last_error(), "multiple of P") == NULL) return 4;
+  int32_t tq = 0, tk = 0;
+  if (ra_tile_shape(RA_BF16, 128, &tq, &tk) != RA_OK || tq <= 0 || tk <= 0) return 5;
+  if (ra_tile_shape(RA_BF16, 96, &tq, &tk) != RA_E_UNSUPPORTED) return 6;
+  printf("ok %d %d\n", tq, tk);
+  return 0;
+}
+''')
+    exe = tmp_path / "use_ra"
+    libdir = os.path.join(ROOT, "striped_blockwise_amd")
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), str(src),
+                    "-L", libdir, "-lra", f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0, (out.returncode, out.stdout, out.stderr)
+    assert out.stdout.startswith("ok ")
