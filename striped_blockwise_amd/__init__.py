@@ -458,3 +458,21 @@ def permute_rope(x: torch.Tensor, P: int, layout="striped", pos=None, base: floa
                                      _layout(layout), float(base), int(style), 1 if inverse else 0,
                                      _vp(_stream(x.device))), "ra_permute_rope")
     return out
+
+
+# The C entry points' own names, for callers who follow include/ra.h (ra_last_error is reported
+# inside the exceptions instead).
+ra_abi_version = abi_version
+ra_check = check
+ra_tile_shape = tile_shape
+ra_permute = permute
+ra_permute_ids = permute_ids
+ra_permute_rope = permute_rope
+ra_round = round
+ra_merge = merge
+ra_forward = forward
+ra_bwd_delta = bwd_delta
+ra_backward_round = backward_round
+ra_backward = backward
+__all__ += ["ra_abi_version", "ra_check", "ra_tile_shape", "ra_permute", "ra_permute_ids", "ra_permute_rope",
+            "ra_round", "ra_merge", "ra_forward", "ra_bwd_delta", "ra_backward_round", "ra_backward"]

@@ -223,3 +223,16 @@ int main(void) {
     out = subprocess.run([str(exe)], capture_output=True, text=True)
     assert out.returncode == 0, (out.returncode, out.stdout, out.stderr)
     assert out.stdout.startswith("ok ")
+
+
+def test_binding_offers_every_c_entry_point_by_name(ra):
+    """Every function the header declares has a binding of the same name (ra_last_error's text
+    arrives in the exceptions)."""
+    import re as _re
+    names = _re.findall(r"^\S.*?\b(ra_\w+)\(", open(os.path.join(ROOT, "include", "ra.h")).read(), _re.M)
+    assert names, "no declarations found"
+    for name in names:
+        if name == "ra_last_error":
+            continue
+        assert callable(getattr(ra, name, None)), name
+        assert name in ra.__all__, name
