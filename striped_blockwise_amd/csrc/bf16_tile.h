@@ -155,8 +155,26 @@ __device__ __forceinline__ void dma_issue(const unsigned* voff, const char* bloc
   }
 }
 
+// The same transposed read with the tile pointer marked restrict.  After inlining, the two reads
+// then carry alias-scope metadata, and the compiler's wait-count pass no longer makes them wait
+// for every LDS DMA still in flight (it does so for LDS reads that carry no alias information).
+// The caller must itself wait for the DMA that filled `tile` (vm_wait) before the call.
+__device__ __forceinline__ bf16x8 read_a_tr_nowait(const char* __restrict__ tile, int off_lo, int off_hi) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off_lo));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off_hi));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// s_waitcnt with vmcnt(N) only (expcnt and lgkmcnt left at their maxima): at most N of this
+// thread's vector-memory loads, LDS DMA included, still outstanding.  They complete in order.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 __device__ __forceinline__ void wait_dma_and_barrier() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's LDS DMA has landed
+  vm_wait<0>();                         // this thread's LDS DMA has landed
   __syncthreads();
 }
 

@@ -1,9 +1,11 @@
 // bf16 blockwise attention on gfx950 matrix cores (v_mfma_f32_32x32x16_bf16), head dim 128.
 //
-// What one workgroup computes: NW wavefronts x QW query rows of device p's Q block (NW = 12,
-// or 4 when the grid would not give every CU two workgroups), against
-// the K/V blocks of the ring rounds it is given (Ring Attention review, step 2: round r brings
-// the block of device (p - r) mod P), folding each round in with the online softmax (step 3).
+// What one workgroup computes: NR row groups of QW query rows of device p's Q block, against the
+// K/V blocks of the ring rounds it is given (Ring Attention review, step 2: round r brings the
+// block of device (p - r) mod P), folding each round in with the online softmax (step 3).  Each
+// row group's key tiles are spread over NS wavefronts (key splits) whose partial states are
+// merged at the end, so a workgroup has NR NS wavefronts: 12 x 1 for grids with at least two
+// such workgroups per CU, and split shapes for smaller grids (see launch_attn_bf16).
 // Masks follow the GetMask procedures of the Striped Attention review ("GetMask 函数"), applied
 // per tile: a tile with no visible pair is skipped ("分块与分瓦片"), a tile with every pair
 // visible runs unmasked, and only tiles that straddle the diagonal pay for an element mask.
@@ -12,8 +14,8 @@
 //   HBM -> LDS by DMA (buffer_load ... lds, 16 B per lane), K and V both row-major with a
 //   per-row XOR swizzle of their 16-byte chunks; no registers or VALU work on the way in.  A
 //   block's rows are consecutive in HBM, or P rows apart when a striped block is read straight
-//   from a token-order tensor (row y of block k is token y P + k).  Two LDS stages: the next
-//   tile's load is in flight while this tile computes.
+//   from a token-order tensor (row y of block k is token y P + k).  Two or three LDS stages per
+//   key split: the next tiles' loads are in flight while this tile computes.
 //   S^T = K Q^T on MFMA: A = 32 K rows from LDS, B = the wavefront's Q columns in registers.
 //   In this orientation each lane owns one query, so the row max / row sum are in-lane
 //   reductions plus one v_permlane32_swap with the other half of the wavefront.
@@ -39,9 +41,6 @@ using namespace bf16t;
 
 #ifndef RA_BF16_NW
 #define RA_BF16_NW 12           // wavefronts per workgroup (one workgroup fills a CU at 3 waves per SIMD)
-#endif
-#ifndef RA_BF16_NW_SMALL
-#define RA_BF16_NW_SMALL 4      // wavefronts per workgroup for grids that do not fill the chip
 #endif
 #ifndef RA_BF16_XMAP
 #define RA_BF16_XMAP 1          // 1: XCD-major block order (one (head, device) stream per XCD)
@@ -74,39 +73,54 @@ constexpr float LAZY_LIM = 4096.0f;   // 2^(TAU + 4)
 // the chunk index.  K tiles are only read row-wise (MFMA A operand), V tiles only transposed
 // (ds_read_b64_tr_b16), so each gets the mask that is conflict-free for its own read pattern.
 
-template <int QB, int TK, bool STATS, int NW>
+// Workgroup shape: NR row groups of QW queries times NS key splits, NW = NR NS wavefronts.  The
+// NR wavefronts of a split share its K/V tiles (one DMA, one LDS copy); split s takes tiles s,
+// s + NS, s + 2 NS, ... of every round, so a row group's sweep over its keys is spread over NS
+// wavefronts, whose partial softmax states are merged through LDS at the end (the same rule as
+// the log-sum-exp merge of "Computing Attention Weights in Sequence Parallelism": rescale both
+// to the larger reference, add numerators and denominators).  NST LDS stages per split: NST - 1
+// tiles in flight while one computes.
+template <int QB, int TK, bool STATS, int NR, int NS, int NST>
 struct Attn {
+  static constexpr int NW = NR * NS;              // wavefronts per workgroup
   static constexpr int QW = 32 * QB;              // query rows per wavefront
-  static constexpr int TQ = NW * QW;              // query rows per workgroup
+  static constexpr int TQ = NR * QW;              // query rows per workgroup
   static constexpr int KB = TK / 32;              // 32-key MFMA blocks per tile
   static constexpr int KS = TK / 16;              // 16-key MFMA k-steps per tile (P V)
   static constexpr int TILE = TK * ROWB;          // bytes of one K or V tile
+  static constexpr int SPLIT_BYTES = 2 * NST * TILE;              // K stages, then V stages
+  static constexpr int SLOT = QB * (64 * 64 * 4 + 2 * 64 * 4);    // one wavefront's O, m, l
+  static constexpr int MERGE_BYTES = (NS - 1) * NR * SLOT;
+  static constexpr int LDS_BYTES = NS * SPLIT_BYTES > MERGE_BYTES ? NS * SPLIT_BYTES : MERGE_BYTES;
+  static_assert(NST == 2 || NST == 3, "two or three stages");
 
-  // Per-lane constant parts of the LDS addresses.
+  // Per-lane constant parts of the LDS addresses (split base included).
   int k_base[8];       // K operand: row l32, chunk (2 dk + hh)
   int v_base[4][2];    // V^T operand: transposed reads, [d-block][first/second 4 keys]
 
-  __device__ __forceinline__ void init_offsets(int lane) {
+  __device__ __forceinline__ void init_offsets(int lane, int split_base) {
 #pragma unroll
-    for (int dk = 0; dk < 8; ++dk) k_base[dk] = a_rowwise_off<SWZ_K>(lane, dk);
+    for (int dk = 0; dk < 8; ++dk) k_base[dk] = split_base + a_rowwise_off<SWZ_K>(lane, dk);
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int sec = 0; sec < 2; ++sec) v_base[db][sec] = a_tr_off<SWZ_V>(lane, db, sec);
+      for (int sec = 0; sec < 2; ++sec) v_base[db][sec] = split_base + a_tr_off<SWZ_V>(lane, db, sec);
   }
 };
 
-template <int QB, int TK, bool STATS, int NW>
-__global__ __launch_bounds__(NW * 64, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) {
-  using A = Attn<QB, TK, STATS, NW>;
-  constexpr int QW = A::QW, TQ = A::TQ, KB = A::KB, KS = A::KS, TILE = A::TILE;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];   // K0 K1 V0 V1
-  auto kst = [&](int i) __attribute__((always_inline)) { return smem + (i & 1) * TILE; };
-  auto vst = [&](int i) __attribute__((always_inline)) { return smem + (2 + (i & 1)) * TILE; };
+template <int QB, int TK, bool STATS, int NR, int NS, int NST>
+__global__ __launch_bounds__(NR * NS * 64, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) {
+  using A = Attn<QB, TK, STATS, NR, NS, NST>;
+  constexpr int NW = A::NW, QW = A::QW, TQ = A::TQ, KB = A::KB, KS = A::KS, TILE = A::TILE;
+  __shared__ __attribute__((aligned(1024))) char smem[A::LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = NS == 1 ? wave_u : wave_u % NR;   // row group
+  const int s = NS == 1 ? 0 : wave_u / NR;        // key split
+  const int split_base = s * A::SPLIT_BYTES;
+  char* const sb = smem + split_base;             // this split's stages
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const int c = a.c;
@@ -141,15 +155,15 @@ __global__ __launch_bounds__(NW * 64, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) 
   const int p = a.p_begin + dev;
   const int q_wg0 = qt * TQ;
   const int q_wg_last = min(c, q_wg0 + TQ) - 1;
-  const int qw0 = q_wg0 + wave_u * QW;
+  const int qw0 = q_wg0 + g * QW;
   const int qw_last = min(c, qw0 + QW) - 1;  // < qw0 when the wave has no rows
   const bool wave_live = qw0 < c;
 
   A off;
-  off.init_offsets(lane);
-  unsigned kdma[DmaShape<NW, TK>::PER_WAVE], vdma[DmaShape<NW, TK>::PER_WAVE];
-  dma_init<NW, TK>(kdma, SWZ_K, wave_u, lane, a.row_step);
-  dma_init<NW, TK>(vdma, SWZ_V, wave_u, lane, a.row_step);
+  off.init_offsets(lane, split_base);
+  unsigned kdma[DmaShape<NR, TK>::PER_WAVE], vdma[DmaShape<NR, TK>::PER_WAVE];
+  dma_init<NR, TK>(kdma, SWZ_K, g, lane, a.row_step);
+  dma_init<NR, TK>(vdma, SWZ_V, g, lane, a.row_step);
 
   // ---- Q columns (B operand): lane holds row qw0 + 32 qb + l32, head dims 16 dk + 8 hh .. +7
   const __bf16* qp = (const __bf16*)a.q + bh * a.q_bh_stride + dev * a.q_dev_stride;
@@ -178,6 +192,9 @@ __global__ __launch_bounds__(NW * 64, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) 
   // more registers than the 3-waves-per-SIMD budget leaves.  The counting variant, which holds
   // more registers and is never timed, keeps the reads next to the MFMAs.
   constexpr int VPRE = STATS ? 0 : RA_BF16_VPRE;
+  // Small workgroups read V^T without the compiler's wait for every LDS DMA in flight (their own
+  // waits cover the tile); measured faster for them and slower for the 12-wave workgroups.
+  constexpr bool TR_NOWAIT = NW <= 8;
 
   // S^T tile of one wavefront: [qb][32-key block]
   f32x16 sA[QB][KB];
@@ -211,7 +228,8 @@ __global__ __launch_bounds__(NW * 64, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) 
       for (int ks = ks0; ks < ks1; ++ks)
 #pragma unroll
         for (int db = 0; db < 4; ++db)
-          va[ks][db] = read_a_tr(vs_ + ks * 16 * ROWB, off.v_base[db][0], off.v_base[db][1]);
+          va[ks][db] = TR_NOWAIT ? read_a_tr_nowait(vs_ + ks * 16 * ROWB, off.v_base[db][0], off.v_base[db][1])
+                                 : read_a_tr(vs_ + ks * 16 * ROWB, off.v_base[db][0], off.v_base[db][1]);
       __builtin_amdgcn_sched_barrier(0);
     };
     if (VPRE == 2) read_v(0, KS);
@@ -303,7 +321,9 @@ __global__ __launch_bounds__(NW * 64, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) 
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        if (VPRE == 0) va[ks][db] = read_a_tr(vs_ + ks * 16 * ROWB, off.v_base[db][0], off.v_base[db][1]);
+        if (VPRE == 0)
+          va[ks][db] = TR_NOWAIT ? read_a_tr_nowait(vs_ + ks * 16 * ROWB, off.v_base[db][0], off.v_base[db][1])
+                                 : read_a_tr(vs_ + ks * 16 * ROWB, off.v_base[db][0], off.v_base[db][1]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks][db], pf[qb][ks], o[qb][db], 0, 0, 0);
@@ -312,6 +332,12 @@ __global__ __launch_bounds__(NW * 64, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) 
   };
 
   const int ntk_all = (c + TK - 1) / TK;
+  // tiles of [0, n) that split s takes (s, s + NS, ...)
+  auto split_count = [&](int n) -> int { return NS == 1 ? n : (n > s ? (n - s + NS - 1) / NS : 0); };
+  // Loads per tile and wavefront (K and V) for the partial wait of a three-stage pipeline; every
+  // wavefront of a split then issues the same number.
+  constexpr int LPT = 2 * DmaShape<NR, TK>::PER_WAVE;
+  static_assert(NST == 2 || DmaShape<NR, TK>::SEGS % NR == 0, "uneven DMA shares");
   for (int rr = 0; rr < a.r_count; ++rr) {
     const int r = a.r_begin + rr;
     const int k = ring_block(p, r, a.P);
@@ -361,32 +387,81 @@ __global__ __launch_bounds__(NW * 64, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) 
       }
     };
 
-    if (ntk > 0) {
-      // tile t lives in stage t & 1; its DMA was issued one iteration earlier.  The loop is
-      // unrolled by two so that the stage offsets are compile-time immediates.
-      dma_issue<NW, TK>(kdma, kblk, kst(0), 0, c, a.row_step, wave_u);
-      dma_issue<NW, TK>(vdma, vblk, vst(0), 0, c, a.row_step, wave_u);
-      auto iter = [&](int t, auto stage_c) __attribute__((always_inline)) {
-        constexpr int S = decltype(stage_c)::value;
-        wait_dma_and_barrier();                       // tile t landed; the other stage is free
-        if (t + 1 < ntk) {
-          dma_issue<NW, TK>(kdma, kblk, smem + (1 - S) * TILE, (t + 1) * TK, c, a.row_step, wave_u);
-          dma_issue<NW, TK>(vdma, vblk, smem + (3 - S) * TILE, (t + 1) * TK, c, a.row_step, wave_u);
+    if constexpr (NS == 1 && NST == 2) {
+      // One split, two stages: tile t lives in stage t & 1; its DMA was issued one iteration
+      // earlier.  The loop is unrolled by two so that the stage offsets are compile-time
+      // immediates.
+      if (ntk > 0) {
+        dma_issue<NR, TK>(kdma, kblk, smem, 0, c, a.row_step, g);
+        dma_issue<NR, TK>(vdma, vblk, smem + 2 * TILE, 0, c, a.row_step, g);
+        auto iter = [&](int t, auto stage_c) __attribute__((always_inline)) {
+          constexpr int S = decltype(stage_c)::value;
+          vm_wait<0>();                               // tile t landed; with NR > 1 the barrier
+          if (NR > 1) __syncthreads();                // makes it whole and frees the other stage
+          if (t + 1 < ntk) {
+            dma_issue<NR, TK>(kdma, kblk, smem + (1 - S) * TILE, (t + 1) * TK, c, a.row_step, g);
+            dma_issue<NR, TK>(vdma, vblk, smem + (3 - S) * TILE, (t + 1) * TK, c, a.row_step, g);
+          }
+          const int cls = tile_class(t);
+          if (cls) {
+            compute_s(smem + S * TILE, sA);
+            if (cls >= 2) apply_mask(sA, t, cls == 2);
+            softmax_pv(sA, smem + (2 + S) * TILE);
+          }
+        };
+        int t = 0;
+        for (; t + 1 < ntk; t += 2) {
+          iter(t, std::integral_constant<int, 0>{});
+          iter(t + 1, std::integral_constant<int, 1>{});
         }
-        const int cls = tile_class(t);
-        if (cls) {
-          compute_s(smem + S * TILE, sA);
-          if (cls >= 2) apply_mask(sA, t, cls == 2);
-          softmax_pv(sA, smem + (2 + S) * TILE);
-        }
-      };
-      int t = 0;
-      for (; t + 1 < ntk; t += 2) {
-        iter(t, std::integral_constant<int, 0>{});
-        iter(t + 1, std::integral_constant<int, 1>{});
+        if (t < ntk) iter(t, std::integral_constant<int, 0>{});
+        if (NR > 1) __syncthreads();                  // LDS stages free for the next round
       }
-      if (t < ntk) iter(t, std::integral_constant<int, 0>{});
-      __syncthreads();                                // LDS stages free for the next round
+    } else {
+      // This split's tiles: j = 0 .. my_n - 1 is tile j NS + s.  Wavefronts that share tiles
+      // (NR > 1) run the same iteration count in lock-step; a lone wavefront runs its own.
+      const int my_n = split_count(ntk);
+      const int nit = NR > 1 ? (ntk + NS - 1) / NS : my_n;
+      if (nit > 0) {
+        // my tile j lives in stage j % NST; its DMA was issued NST - 1 iterations earlier.  The
+        // loop is unrolled by NST so that the stage offsets are compile-time immediates.
+        auto issue = [&](int j, int stage) __attribute__((always_inline)) {
+          const int x0 = (j * NS + s) * TK;
+          dma_issue<NR, TK>(kdma, kblk, sb + stage * TILE, x0, c, a.row_step, g);
+          dma_issue<NR, TK>(vdma, vblk, sb + (NST + stage) * TILE, x0, c, a.row_step, g);
+        };
+        // only tiles this split owns: with NR > 1 a split may have none in a round that the
+        // others still iterate over, and its first tile would start past the end of the block
+        if (my_n > 0) issue(0, 0);
+        if (NST == 3 && my_n > 1) issue(1, 1);
+        auto iter = [&](int j, auto stage_c) __attribute__((always_inline)) {
+          constexpr int S = decltype(stage_c)::value;
+          // my tile j landed (with three stages tile j + 1 may stay in flight); with NR > 1 the
+          // barrier makes the whole tile visible and frees the stage read one iteration ago
+          if (NST == 3 && j + 1 < my_n) vm_wait<LPT>();
+          else vm_wait<0>();
+          if (NR > 1) __syncthreads();
+          if (j + NST - 1 < my_n) issue(j + NST - 1, (S + NST - 1) % NST);
+          if (NR == 1 || j < my_n) {
+            const int t = j * NS + s;
+            const int cls = tile_class(t);
+            if (cls) {
+              compute_s(smem + S * TILE, sA);
+              if (cls >= 2) apply_mask(sA, t, cls == 2);
+              softmax_pv(sA, smem + (NST + S) * TILE);
+            }
+          }
+        };
+        int j = 0;
+        for (; j + NST <= nit; j += NST) {
+          iter(j, std::integral_constant<int, 0>{});
+          iter(j + 1, std::integral_constant<int, 1>{});
+          if constexpr (NST == 3) iter(j + 2, std::integral_constant<int, 2>{});
+        }
+        if (j < nit) iter(j, std::integral_constant<int, 0>{});
+        if (NST == 3 && j + 1 < nit) iter(j + 1, std::integral_constant<int, 1>{});
+        if (NR > 1) __syncthreads();                  // LDS stages free for the next round
+      }
     }
 
     if (STATS && wave_live) {
@@ -398,7 +473,55 @@ __global__ __launch_bounds__(NW * 64, RA_BF16_OCC) void k_attn_bf16(AttnArgs a) 
         atomicAdd((unsigned long long*)&st->tiles_full, (unsigned long long)st_full);
         atomicAdd((unsigned long long*)&st->tiles_diag, (unsigned long long)st_diag);
         atomicAdd((unsigned long long*)&st->tiles_skipped,
-                  (unsigned long long)(ntk_all - st_full - st_diag));
+                  (unsigned long long)(split_count(ntk_all) - st_full - st_diag));
+      }
+    }
+  }
+
+  // ---- key splits: splits 1 .. NS-1 hand (m, l, O) to split 0 of their row group through LDS;
+  // split 0 folds them in with the blockwise softmax merge (both sides rescaled to the larger
+  // reference; a side that saw no key has m = -inf and contributes nothing).
+  if constexpr (NS > 1) {
+    __syncthreads();                                  // every split is done with its stages
+    if (s > 0) {
+      char* const slot = smem + ((s - 1) * NR + g) * A::SLOT;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            reinterpret_cast<float4*>(slot)[((qb * 4 + db) * 4 + q4) * 64 + lane] =
+                make_float4(o[qb][db][4 * q4], o[qb][db][4 * q4 + 1], o[qb][db][4 * q4 + 2], o[qb][db][4 * q4 + 3]);
+        float* ml = reinterpret_cast<float*>(slot + QB * 64 * 64 * 4);
+        ml[qb * 128 + lane] = m[qb];
+        ml[qb * 128 + 64 + lane] = l[qb];
+      }
+    }
+    __syncthreads();
+    if (s > 0) return;
+#pragma unroll 1
+    for (int s2 = 1; s2 < NS; ++s2) {
+      const char* const slot = smem + ((s2 - 1) * NR + g) * A::SLOT;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float* ml = reinterpret_cast<const float*>(slot + QB * 64 * 64 * 4);
+        const float m2 = ml[qb * 128 + lane], l2 = ml[qb * 128 + 64 + lane];
+        const float mn = fmaxf(m[qb], m2);
+        const float al = m[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[qb] - mn);
+        const float be = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
+        l[qb] = al * l[qb] + be * l2;
+        m[qb] = mn;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 w = reinterpret_cast<const float4*>(slot)[((qb * 4 + db) * 4 + q4) * 64 + lane];
+            o[qb][db][4 * q4] = al * o[qb][db][4 * q4] + be * w.x;
+            o[qb][db][4 * q4 + 1] = al * o[qb][db][4 * q4 + 1] + be * w.y;
+            o[qb][db][4 * q4 + 2] = al * o[qb][db][4 * q4 + 2] + be * w.z;
+            o[qb][db][4 * q4 + 3] = al * o[qb][db][4 * q4 + 3] + be * w.w;
+          }
       }
     }
   }
@@ -464,32 +587,42 @@ int cu_count() {
   return n;
 }
 
-template <int NW>
-hipError_t launch_nw(const AttnArgs& a, hipStream_t s) {
-  constexpr int TQ = NW * 32 * QB_SEL;
+template <int NR, int NS, int NST>
+hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
+  constexpr int NW = NR * NS;
+  constexpr int TQ = NR * 32 * QB_SEL;
   const int64_t blocks = (int64_t)((a.c + TQ - 1) / TQ) * a.BH * a.n_dev;
   if (blocks * NW * 64 >= (1ll << 32)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks);
   AttnArgs b = a;
   b.xcd_major = ((int64_t)a.BH * a.n_dev) % 8 == 0 ? 1 : 0;
   if (a.stats)
-    hipLaunchKernelGGL((k_attn_bf16<QB_SEL, TK_SEL, true, NW>), grid, dim3(NW * 64), 0, s, b);
+    hipLaunchKernelGGL((k_attn_bf16<QB_SEL, TK_SEL, true, NR, NS, NST>), grid, dim3(NW * 64), 0, s, b);
   else
-    hipLaunchKernelGGL((k_attn_bf16<QB_SEL, TK_SEL, false, NW>), grid, dim3(NW * 64), 0, s, b);
+    hipLaunchKernelGGL((k_attn_bf16<QB_SEL, TK_SEL, false, NR, NS, NST>), grid, dim3(NW * 64), 0, s, b);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Wide workgroups (one per CU, 384 queries sharing each K/V tile) when the grid has at least
-// two of them per CU; otherwise the round lasts as long as one workgroup's sweep over its key
-// tiles, and 4-wave workgroups (one wave per SIMD) sweep about three times faster.
+// Workgroup shape by grid size.  Wide workgroups (one per CU, 384 queries sharing each K/V tile)
+// when the grid has at least two of them per CU.  Below that, a round lasts about as long as the
+// longest sweep of one wavefront over its key tiles, and the smaller the grid the more that sweep
+// is split over wavefronts: with G = 32-row groups of the whole launch and C compute units,
+//   G <= 4 C:   2 row groups x 4 key splits (8 wavefronts, 128 KB LDS, one workgroup per CU),
+//   G <= 12 C:  2 row groups x 2 key splits (4 wavefronts, 64 KB LDS, two per CU),
+//   otherwise:  4 row groups, one split, three LDS stages (4 wavefronts, 48 KB LDS).
+// The same shape serves both layouts: it depends on the grid, not on the mask.
 hipError_t launch_attn_bf16(const AttnArgs& a, int d, hipStream_t s) {
   if (d != D) return hipErrorInvalidValue;
+  const int64_t cus = cu_count();
   constexpr int TQW = RA_BF16_NW * 32 * QB_SEL;
   const int64_t wide = (int64_t)((a.c + TQW - 1) / TQW) * a.BH * a.n_dev;
-  if (wide >= 2 * (int64_t)cu_count()) return launch_nw<RA_BF16_NW>(a, s);
-  return launch_nw<RA_BF16_NW_SMALL>(a, s);
+  if (wide >= 2 * cus) return launch_cfg<RA_BF16_NW, 1, 2>(a, s);
+  const int64_t groups = (int64_t)((a.c + 32 * QB_SEL - 1) / (32 * QB_SEL)) * a.BH * a.n_dev;
+  if (groups <= 4 * cus) return launch_cfg<2, 4, 2>(a, s);
+  if (groups <= 12 * cus) return launch_cfg<2, 2, 2>(a, s);
+  return launch_cfg<4, 1, 3>(a, s);
 }
 
 }  // namespace ra

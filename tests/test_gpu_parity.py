@@ -385,7 +385,42 @@ def test_wide_workgroup_path(ra, layout):
             compare(po[0, h], pl[0, h], ro, rl, "bf16", f"wide round p={p} kv={kk} h={h}")
 
 
-@pytest.mark.parametrize("H", [2, 128])          # 4-wave and 12-wave workgroups
+@pytest.mark.parametrize("H,P,c", [(2, 4, 1000), (64, 2, 600), (96, 2, 700)])
+def test_small_grid_workgroup_shapes(ra, H, P, c):
+    """Grids below two 12-wave workgroups per CU pick their workgroup shape by the number of
+    32-row groups G in the launch; on a 256-CU device these three cases take 2 row groups x 4 key
+    splits (G = 256), 2 x 2 (G = 2432) and 4 row groups with three LDS stages (G = 4224), all
+    with a ragged last tile.  The split workgroups merge their partial softmax states in LDS;
+    element-wise against the oracle on three heads, counters on all, and one round per direction
+    (whose single-device grids take the split shapes too)."""
+    B, d = 1, 128
+    n = P * c
+    g = torch.Generator().manual_seed(4100 + H + c)
+    q, k, v = (torch.randn((B, H, n, d), generator=g).mul(0.5).to(torch.bfloat16) for _ in range(3))
+    heads = [0, 1, H - 1]
+    qh, kh, vh = (t[:, heads] for t in (q, k, v))
+    tq, tk = ra.tile_shape(ra.BF16, d)
+    for layout in ("contiguous", "striped"):
+        (ql, kl, vl), order = _oracle_layout((qh, kh, vh), P, layout)
+        o_ref, l_ref = OA.attention(ql, kl, vl, True, pos_q=order, pos_k=order)
+        qg, kg, vg = (ra.permute(t.cuda(), P) if layout == "striped" else t.cuda() for t in (q, k, v))
+        stats = ra.new_stats(P)
+        o, lse = ra.forward(qg, kg, vg, P, layout, True, o_dtype=torch.float32, stats=stats)
+        torch.cuda.synchronize()
+        idx = torch.tensor(heads, device="cuda")
+        compare(o.index_select(1, idx), lse.index_select(1, idx), o_ref, l_ref, "bf16", f"H={H} c={c} {layout}")
+        assert np.array_equal(stats.cpu().numpy(), _expected_stats(layout, P, c, B * H, True, tq, tk))
+        for p, kk in ((P - 1, 0), (0, P - 1)):
+            po, pl = ra.round(qg[:, :, p * c:(p + 1) * c], kg[:, :, kk * c:(kk + 1) * c], vg[:, :, kk * c:(kk + 1) * c],
+                              P, p, kk, layout, True)
+            torch.cuda.synchronize()
+            for jj, h in enumerate(heads):
+                ro, rl = OR.round_partial(ql[0, jj, p * c:(p + 1) * c], kl[0, jj, kk * c:(kk + 1) * c],
+                                          vl[0, jj, kk * c:(kk + 1) * c], layout, p, kk, True)
+                compare(po[0, h], pl[0, h], ro, rl, "bf16", f"H={H} c={c} {layout} round p={p} kv={kk} h={h}")
+
+
+@pytest.mark.parametrize("H", [2, 128])          # split and 12-wave workgroups
 def test_rising_scores_take_the_rescale_path(ra, H):
     """Scores that grow with the key position by about 3 log2 units per 32-key tile (more for
     some heads), so that the running reference falls behind again and again and the kernel's
@@ -415,8 +450,8 @@ def test_rising_scores_take_the_rescale_path(ra, H):
 @pytest.mark.parametrize("H,c", [(256, 383), (256, 384), (256, 385), (2, 127), (2, 128), (2, 129)])
 def test_workgroup_tile_boundaries(ra, H, c):
     """Block sizes at and around a workgroup's query tile: 384 rows for the 12-wave kernel (the
-    256-head cases, whose grids of at least two 12-wave workgroups per CU select it) and 128 rows
-    for the 4-wave kernel."""
+    256-head cases, whose grids of at least two 12-wave workgroups per CU select it), and around
+    four 32-key tiles, one per key split of the small-grid workgroups (the 2-head cases)."""
     B, P, d = 1, 2, 128
     n = P * c
     g = torch.Generator().manual_seed(7000 + c + H)
