@@ -187,9 +187,10 @@ def per_round_all_devices(torch, ra, dev, name: str = "seq_n8k", reps: int = 5):
 
 def sweep(torch, ra, dev, P: int = 8, H: int = 8, d: int = 128,
           lengths=(16384, 32768, 65536, 131072, 262144, 524288, 1048576)) -> int:
-    """Fused-forward time of the last device (most causal work under the contiguous layout)
-    for both layouts as the sequence grows: the attention-only version of the Striped
-    Attention review's speedup-vs-length table (which measures whole training steps)."""
+    """Fused-forward and backward time of the last device (most causal work under the
+    contiguous layout) for both layouts as the sequence grows: the attention-only version of
+    the Striped Attention review's speedup-vs-length table (which measures whole training
+    steps).  The backward is ra_backward with D precomputed, as in the default line's field."""
     rows = []
     for n in lengths:
         c = n // P
@@ -200,29 +201,44 @@ def sweep(torch, ra, dev, P: int = 8, H: int = 8, d: int = 128,
         qs, ks, vs = (ra.permute(t, P) for t in (q, k, v))
         o = torch.empty((1, H, c, d), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((1, H, c), dtype=torch.float32, device=dev)
+        dout = torch.randn((1, H, c, d), generator=gen, device=dev).to(torch.bfloat16)
+        grads = (torch.empty((1, H, c, d), dtype=torch.float32, device=dev),
+                 torch.empty((1, H, n, d), dtype=torch.float32, device=dev),
+                 torch.empty((1, H, n, d), dtype=torch.float32, device=dev))
         res = {"n": n, "c": c}
-        for layout, args_ in (("contiguous", (q, k, v)), ("striped", (qs, ks, vs))):
-            pairs = sum(useful_pairs(layout, P, c, p))
-            ra.forward(*args_, P, layout, True, p_begin=p, p_end=p + 1, out=(o, lse))
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            reps = max(2, min(20, int(2e13 / (4.0 * d * H * pairs))))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+        def timed(fn, reps):
+            fn()
             torch.cuda.synchronize()
             e0.record()
             for _ in range(reps):
-                ra.forward(*args_, P, layout, True, p_begin=p, p_end=p + 1, out=(o, lse))
+                fn()
             e1.record()
             torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / reps
+            return e0.elapsed_time(e1) / reps
+
+        for layout, args_ in (("contiguous", (q, k, v)), ("striped", (qs, ks, vs))):
+            pairs = sum(useful_pairs(layout, P, c, p))
+            reps = max(2, min(20, int(2e13 / (4.0 * d * H * pairs))))
+            ms = timed(lambda: ra.forward(*args_, P, layout, True, p_begin=p, p_end=p + 1, out=(o, lse)), reps)
             res[layout + "_ms"] = round(ms, 4)
             res[layout + "_tflops"] = round(4.0 * d * H * pairs / (ms * 1e-3) / 1e12, 1)
+            delta = ra.bwd_delta(o, dout)
+            ms = timed(lambda: ra.backward(*args_, dout, lse, P, layout, True, p, p + 1, delta=delta, out=grads),
+                       max(2, reps // 3))
+            res["bwd_" + layout + "_ms"] = round(ms, 4)
+            res["bwd_" + layout + "_tflops"] = round(10.0 * d * H * pairs / (ms * 1e-3) / 1e12, 1)
         res["speedup"] = round(res["contiguous_ms"] / res["striped_ms"], 4)
+        res["bwd_speedup"] = round(res["bwd_contiguous_ms"] / res["bwd_striped_ms"], 4)
         res["ideal_speedup"] = round(sum(useful_pairs("contiguous", P, c, p)) / sum(useful_pairs("striped", P, c, p)), 5)
-        log(f"[sweep] n={n}: contiguous {res['contiguous_ms']:.3f} ms, striped {res['striped_ms']:.3f} ms, "
-            f"speedup {res['speedup']:.3f} (ideal {res['ideal_speedup']})")
+        log(f"[sweep] n={n}: forward contiguous {res['contiguous_ms']:.3f} ms, striped {res['striped_ms']:.3f} ms, "
+            f"speedup {res['speedup']:.3f}; backward {res['bwd_contiguous_ms']:.3f} / {res['bwd_striped_ms']:.3f} ms, "
+            f"speedup {res['bwd_speedup']:.3f} (ideal {res['ideal_speedup']})")
         rows.append(res)
-        del q, k, v, qs, ks, vs, o, lse
+        del q, k, v, qs, ks, vs, o, lse, dout, grads
         torch.cuda.empty_cache()
-    print(json.dumps({"metric": "striped/ring attention-only speedup vs sequence length, 1 GPU",
+    print(json.dumps({"metric": "striped/ring attention-only speedup vs sequence length (forward, backward), 1 GPU",
                       "config": {"P": P, "device": P - 1, "B": 1, "H": H, "d": d, "dtype": "bf16",
                                  "data": "synthetic N(0,1)*0.5 (GPU generator)"},
                       "sweep": rows}), flush=True)

@@ -28,7 +28,6 @@
 // because O, l and the reference max always stay consistent.  The tile max itself is only
 // computed when P against the current reference comes out large (a lane's partial row sum
 // above 2^12) or a row has no reference yet; otherwise that first P is kept.
-#include <atomic>
 #include <type_traits>
 
 #include "bf16_tile.h"
@@ -572,20 +571,6 @@ bool attn_bf16_supported(int64_t d) { return d == D; }
 void attn_bf16_tile(int* tq, int* tk) { *tq = 32 * QB_SEL; *tk = TK_SEL; }
 
 namespace {
-
-// Compute units of the current device (queried once per device; concurrent first calls from
-// several host threads store the same value).
-int cu_count() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int n = cached[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
 
 template <int NR, int NS, int NST>
 hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {

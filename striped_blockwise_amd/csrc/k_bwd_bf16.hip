@@ -102,14 +102,26 @@ __device__ __forceinline__ void store_rows(float* row, const f32x16 (&acc)[4], f
 }
 
 // ------------------------------------------------------------------------------- dQ kernel
-__global__ __launch_bounds__(RA_BWD_DQ_NW * 64, 2) void k_bwd_dq_bf16(BwdArgs a) {
-  constexpr int NW = RA_BWD_DQ_NW;
-  constexpr int WG_ROWS = NW * WR;      // stationary rows per workgroup
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];   // K0 K1 V0 V1
+// NR row groups of WR query rows times NS key splits (NR NS wavefronts).  With NS > 1, split s
+// of a row group takes the K/V tiles s, s + NS, ... of every round into LDS stages of its own
+// (shared by its NR wavefronts), and the splits' dQ partial sums are added up through LDS at the
+// end: grids too small to fill the chip then spread each row group's sweep over its keys.
+template <int NR, int NS>
+__global__ __launch_bounds__(NR * NS * 64, 2) void k_bwd_dq_bf16(BwdArgs a) {
+  constexpr int NW = NR * NS;
+  constexpr int WG_ROWS = NR * WR;      // stationary rows per workgroup
+  constexpr int SPLIT_BYTES = 4 * TILE;                       // K0 K1 V0 V1 of one split
+  constexpr int SLOT = 64 * 64 * 4;                           // one wavefront's dQ partial
+  constexpr int LDS_BYTES = NS * SPLIT_BYTES > (NS - 1) * NR * SLOT ? NS * SPLIT_BYTES : (NS - 1) * NR * SLOT;
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = NS == 1 ? wave_u : wave_u % NR;   // row group
+  const int s = NS == 1 ? 0 : wave_u / NR;        // key split
+  const int split_base = s * SPLIT_BYTES;
+  char* const sb = smem + split_base;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const int c = a.c;
@@ -121,7 +133,7 @@ __global__ __launch_bounds__(RA_BWD_DQ_NW * 64, 2) void k_bwd_dq_bf16(BwdArgs a)
   const int dev = stream / a.BH;
   const int p = a.p_begin + dev;
   const int q_wg_last = min(c, qt * WG_ROWS + WG_ROWS) - 1;
-  const int qw0 = qt * WG_ROWS + wave_u * WR;
+  const int qw0 = qt * WG_ROWS + g * WR;
   const int qw_last = min(c, qw0 + WR) - 1;
   const bool wave_live = qw0 < c;
   const int y = qw0 + l32;
@@ -129,16 +141,19 @@ __global__ __launch_bounds__(RA_BWD_DQ_NW * 64, 2) void k_bwd_dq_bf16(BwdArgs a)
   int k_row[8], v_row[8], k_tr[4][2];
 #pragma unroll
   for (int dk = 0; dk < 8; ++dk) {
-    k_row[dk] = a_rowwise_off<SWZ_T>(lane, dk);
-    v_row[dk] = a_rowwise_off<SWZ_K>(lane, dk);
+    k_row[dk] = split_base + a_rowwise_off<SWZ_T>(lane, dk);
+    v_row[dk] = split_base + a_rowwise_off<SWZ_K>(lane, dk);
   }
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int sec = 0; sec < 2; ++sec) k_tr[db][sec] = a_tr_off<SWZ_T>(lane, db, sec);
-  unsigned kdma[DmaShape<NW, TS>::PER_WAVE], vdma[DmaShape<NW, TS>::PER_WAVE];
-  dma_init<NW, TS>(kdma, SWZ_T, wave_u, lane, a.row_step);
-  dma_init<NW, TS>(vdma, SWZ_K, wave_u, lane, a.row_step);
+    for (int sec = 0; sec < 2; ++sec) k_tr[db][sec] = split_base + a_tr_off<SWZ_T>(lane, db, sec);
+  unsigned kdma[DmaShape<NR, TS>::PER_WAVE], vdma[DmaShape<NR, TS>::PER_WAVE];
+  dma_init<NR, TS>(kdma, SWZ_T, g, lane, a.row_step);
+  dma_init<NR, TS>(vdma, SWZ_K, g, lane, a.row_step);
+  // Split workgroups read K^T without the compiler's wait for every LDS DMA in flight (their
+  // own waits cover the tile), as the forward's small shapes do.
+  constexpr bool TR_NOWAIT = NS > 1;
 
   // B operands: this lane's query row of Q and dO, head dims 16 dk + 8 hh .. +7
   const int64_t rstride = (int64_t)a.row_step * D;   // elements between rows of a block
@@ -221,32 +236,97 @@ __global__ __launch_bounds__(RA_BWD_DQ_NW * 64, 2) void k_bwd_dq_bf16(BwdArgs a)
       const bf16x8 ds1 = pack8(ds, 1);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const bf16x8 k0 = read_a_tr(ks_, k_tr[db][0], k_tr[db][1]);
+        const bf16x8 k0 = TR_NOWAIT ? read_a_tr_nowait(ks_, k_tr[db][0], k_tr[db][1])
+                                    : read_a_tr(ks_, k_tr[db][0], k_tr[db][1]);
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, ds0, acc[db], 0, 0, 0);
-        const bf16x8 k1 = read_a_tr(ks_ + 16 * ROWB, k_tr[db][0], k_tr[db][1]);
+        const bf16x8 k1 = TR_NOWAIT ? read_a_tr_nowait(ks_ + 16 * ROWB, k_tr[db][0], k_tr[db][1])
+                                    : read_a_tr(ks_ + 16 * ROWB, k_tr[db][0], k_tr[db][1]);
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, ds1, acc[db], 0, 0, 0);
       }
     };
 
-    dma_issue<NW, TS>(kdma, kblk, smem, 0, c, a.row_step, wave_u);
-    dma_issue<NW, TS>(vdma, vblk, smem + 2 * TILE, 0, c, a.row_step, wave_u);
-    auto iter = [&](int t, auto stage_c) __attribute__((always_inline)) {
-      constexpr int S = decltype(stage_c)::value;
-      wait_dma_and_barrier();                         // tile t landed; the other stage is free
-      if (t + 1 < ntk) {
-        dma_issue<NW, TS>(kdma, kblk, smem + (1 - S) * TILE, (t + 1) * TS, c, a.row_step, wave_u);
-        dma_issue<NW, TS>(vdma, vblk, smem + (3 - S) * TILE, (t + 1) * TS, c, a.row_step, wave_u);
+    if constexpr (NS == 1) {
+      dma_issue<NR, TS>(kdma, kblk, smem, 0, c, a.row_step, g);
+      dma_issue<NR, TS>(vdma, vblk, smem + 2 * TILE, 0, c, a.row_step, g);
+      auto iter = [&](int t, auto stage_c) __attribute__((always_inline)) {
+        constexpr int S = decltype(stage_c)::value;
+        wait_dma_and_barrier();                       // tile t landed; the other stage is free
+        if (t + 1 < ntk) {
+          dma_issue<NR, TS>(kdma, kblk, smem + (1 - S) * TILE, (t + 1) * TS, c, a.row_step, g);
+          dma_issue<NR, TS>(vdma, vblk, smem + (3 - S) * TILE, (t + 1) * TS, c, a.row_step, g);
+        }
+        const int cls = tile_class(t);
+        if (cls) compute(smem + S * TILE, smem + (2 + S) * TILE, t, cls == 2);
+      };
+      int t = 0;
+      for (; t + 1 < ntk; t += 2) {
+        iter(t, std::integral_constant<int, 0>{});
+        iter(t + 1, std::integral_constant<int, 1>{});
       }
-      const int cls = tile_class(t);
-      if (cls) compute(smem + S * TILE, smem + (2 + S) * TILE, t, cls == 2);
-    };
-    int t = 0;
-    for (; t + 1 < ntk; t += 2) {
-      iter(t, std::integral_constant<int, 0>{});
-      iter(t + 1, std::integral_constant<int, 1>{});
+      if (t < ntk) iter(t, std::integral_constant<int, 0>{});
+      __syncthreads();                                // LDS stages free for the next round
+    } else {
+      // This split's tiles: j = 0 .. my_n - 1 is tile j NS + s, in stage j & 1.  Wavefronts that
+      // share tiles (NR > 1) run the workgroup's iteration count in lock-step; a lone wavefront
+      // runs its own.  Only owned tiles are fetched: a split may own none in a round.
+      const int my_n = ntk > s ? (ntk - s + NS - 1) / NS : 0;
+      const int nit = NR > 1 ? (ntk + NS - 1) / NS : my_n;
+      auto issue = [&](int j, int stage) __attribute__((always_inline)) {
+        const int x0 = (j * NS + s) * TS;
+        dma_issue<NR, TS>(kdma, kblk, sb + stage * TILE, x0, c, a.row_step, g);
+        dma_issue<NR, TS>(vdma, vblk, sb + (2 + stage) * TILE, x0, c, a.row_step, g);
+      };
+      if (my_n > 0) issue(0, 0);
+      auto iter = [&](int j, auto stage_c) __attribute__((always_inline)) {
+        constexpr int S = decltype(stage_c)::value;
+        vm_wait<0>();                                 // my tile j landed; with NR > 1 the
+        if (NR > 1) __syncthreads();                  // barrier also frees the other stage
+        if (j + 1 < my_n) issue(j + 1, 1 - S);
+        if (NR == 1 || j < my_n) {
+          const int t = j * NS + s;
+          const int cls = tile_class(t);
+          if (cls) compute(smem + S * TILE, smem + (2 + S) * TILE, t, cls == 2);
+        }
+      };
+      int j = 0;
+      for (; j + 1 < nit; j += 2) {
+        iter(j, std::integral_constant<int, 0>{});
+        iter(j + 1, std::integral_constant<int, 1>{});
+      }
+      if (j < nit) iter(j, std::integral_constant<int, 0>{});
+      if (NR > 1) __syncthreads();                    // LDS stages free for the next round
     }
-    if (t < ntk) iter(t, std::integral_constant<int, 0>{});
-    __syncthreads();                                  // LDS stages free for the next round
+  }
+
+  // Key splits: splits 1 .. NS-1 hand their dQ partial sums to split 0 of their row group
+  // through LDS; split 0 adds them up and stores.
+  if constexpr (NS > 1) {
+    __syncthreads();                                  // every split is done with its stages
+    if (s > 0) {
+      float4* const slot = reinterpret_cast<float4*>(smem + ((s - 1) * NR + g) * SLOT);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          slot[(db * 4 + q4) * 64 + lane] =
+              make_float4(acc[db][4 * q4], acc[db][4 * q4 + 1], acc[db][4 * q4 + 2], acc[db][4 * q4 + 3]);
+    }
+    __syncthreads();
+    if (s > 0) return;
+#pragma unroll 1
+    for (int s2 = 1; s2 < NS; ++s2) {
+      const float4* const slot = reinterpret_cast<const float4*>(smem + ((s2 - 1) * NR + g) * SLOT);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 w = slot[(db * 4 + q4) * 64 + lane];
+          acc[db][4 * q4] += w.x;
+          acc[db][4 * q4 + 1] += w.y;
+          acc[db][4 * q4 + 2] += w.z;
+          acc[db][4 * q4 + 3] += w.w;
+        }
+    }
   }
 
   if (y < c)
@@ -449,6 +529,22 @@ __global__ __launch_bounds__(RA_BWD_DKV_NW * 64, 2) void k_bwd_dkv_bf16(BwdArgs 
 
 bool bwd_bf16_supported(int64_t d) { return d == D; }
 
+namespace {
+
+template <int NR, int NS>
+hipError_t launch_dq(const BwdArgs& a, hipStream_t s) {
+  constexpr int rows = NR * WR, nt = NR * NS * 64;
+  const int64_t nstream = (int64_t)a.BH * a.n_dev;
+  const int64_t blocks = (a.c + rows - 1) / rows * nstream;
+  if (blocks * nt >= (1ll << 32)) return hipErrorInvalidConfiguration;
+  BwdArgs b = a;
+  b.xcd_major = nstream % 8 == 0 ? 1 : 0;
+  hipLaunchKernelGGL((k_bwd_dq_bf16<NR, NS>), dim3((unsigned)blocks), dim3(nt), 0, s, b);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_bwd_bf16(const BwdArgs& a, int d, bool dq, bool dkv, hipStream_t s) {
   if (d != D) return hipErrorInvalidValue;
   if (dkv) {
@@ -463,14 +559,16 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int d, bool dq, bool dkv, hipStream
     if (e != hipSuccess) return e;
   }
   if (dq) {
-    constexpr int rows = RA_BWD_DQ_NW * WR, nt = RA_BWD_DQ_NW * 64;
-    const int64_t nstream = (int64_t)a.BH * a.n_dev;
-    const int64_t blocks = (a.c + rows - 1) / rows * nstream;
-    if (blocks * nt >= (1ll << 32)) return hipErrorInvalidConfiguration;
-    BwdArgs b = a;
-    b.xcd_major = nstream % 8 == 0 ? 1 : 0;
-    hipLaunchKernelGGL(k_bwd_dq_bf16, dim3((unsigned)blocks), dim3(nt), 0, s, b);
-    return hipGetLastError();
+    // dQ workgroup shape by grid size: 8-wave workgroups when there are at least two per CU;
+    // below that, with G = 32-row groups in the launch and C compute units, 2 row groups x 4 key
+    // splits up to G = 4 C, else 4 x 2 (each split with its own two K/V stages in LDS).
+    const int64_t cus = cu_count();
+    constexpr int WIDE_ROWS = RA_BWD_DQ_NW * WR;
+    const int64_t wide = (int64_t)((a.c + WIDE_ROWS - 1) / WIDE_ROWS) * a.BH * a.n_dev;
+    if (wide >= 2 * cus) return launch_dq<RA_BWD_DQ_NW, 1>(a, s);
+    const int64_t groups = (int64_t)((a.c + WR - 1) / WR) * a.BH * a.n_dev;
+    if (groups <= 4 * cus) return launch_dq<2, 4>(a, s);
+    return launch_dq<4, 2>(a, s);
   }
   return hipSuccess;
 }

@@ -1,11 +1,30 @@
 // Host side of libra.so: argument validation, error reporting and kernel dispatch for the C ABI
 // declared in include/ra.h.  Nothing here allocates device memory or synchronizes.
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 
 #include "ra_internal.h"
+
+namespace ra {
+
+// Queried once per device; concurrent first calls from several host threads store the same
+// value.
+int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+}  // namespace ra
 
 namespace {
 

@@ -122,6 +122,9 @@ hipError_t launch_bwd_f32(const BwdArgs& a, int d, bool dq, bool dkv, hipStream_
 hipError_t launch_bwd_bf16(const BwdArgs& a, int d, bool dq, bool dkv, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, int d, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnArgs& a, int d, hipStream_t s);
+// Compute units of the current device (queried once per device), for the launchers' choice of
+// workgroup shape.
+int cu_count();
 
 bool attn_f32_supported(int64_t d);
 bool attn_bf16_supported(int64_t d);

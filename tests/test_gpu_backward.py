@@ -240,8 +240,9 @@ def test_backward_invalid_args(ra):
 
 @pytest.mark.parametrize("c", [127, 129, 255, 257])
 def test_backward_workgroup_boundaries(ra, c):
-    """Block sizes around the backward kernels' workgroup tiles (128 key rows for dK/dV, 256 query
-    rows for dQ), both layouts, against the oracle."""
+    """Block sizes around the backward kernels' workgroup tiles (128 key rows for dK/dV; for dQ,
+    whose small grids take 2 row groups x 4 key splits, around multiples of four 32-key tiles),
+    both layouts, against the oracle."""
     P, H, d = 2, 2, 128
     n = P * c
     gen = torch.Generator().manual_seed(9000 + c)
@@ -252,3 +253,24 @@ def test_backward_workgroup_boundaries(ra, c):
         got = _gpu_fwd_bwd(ra, ql, kl, vl, gl, P, layout, True)
         ref = _oracle(ql, kl, vl, gl, P, order, True)
         _check(got, ref, "bf16", f"c={c} {layout}")
+
+
+@pytest.mark.parametrize("H,P,c", [(2, 4, 1000), (64, 2, 600), (128, 2, 1500)])
+def test_backward_dq_workgroup_shapes(ra, H, P, c):
+    """The dQ kernel picks its workgroup shape by grid size; on a 256-CU device these cases take
+    2 row groups x 4 key splits (2 x 4 x 32 = 256 row groups), 4 x 2 (2432 row groups) and the
+    8-wave workgroups without splits (1536 of them), all with ragged tiles.  The split shapes add
+    their partial dQ sums in LDS.  Gradients of three heads against the oracle, both layouts."""
+    d = 128
+    n = P * c
+    gen = torch.Generator().manual_seed(9500 + H + c)
+    q, k, v, g = (torch.randn((1, H, n, d), generator=gen).mul(0.5 if i < 3 else 1.0).to(torch.bfloat16)
+                  for i in range(4))
+    heads = [0, 1, H - 1]
+    for layout in LAYOUTS:
+        (ql, kl, vl, gl), order = _to_layout((q, k, v, g), P, layout)
+        dq, dk, dv = _gpu_fwd_bwd(ra, ql, kl, vl, gl, P, layout, True)
+        idx = torch.tensor(heads, device="cuda")
+        got = tuple(t.index_select(1, idx) for t in (dq, dk, dv))
+        ref = _oracle(*(t[:, heads].contiguous() for t in (ql, kl, vl, gl)), P, order, True)
+        _check(got, ref, "bf16", f"H={H} c={c} {layout}")
