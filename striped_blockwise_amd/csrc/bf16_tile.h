@@ -173,6 +173,9 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// s_waitcnt lgkmcnt(0) only: this thread's LDS reads have all returned.
+__device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 __device__ __forceinline__ void wait_dma_and_barrier() {
   vm_wait<0>();                         // this thread's LDS DMA has landed
   __syncthreads();

@@ -79,6 +79,14 @@ constexpr float LAZY_LIM = 4096.0f;   // 2^(TAU + 4)
 // the log-sum-exp merge of "Computing Attention Weights in Sequence Parallelism": rescale both
 // to the larger reference, add numerators and denominators).  NST LDS stages per split: NST - 1
 // tiles in flight while one computes.
+//
+// NST = 1 is the paired mode, for launches small enough to be resident at once.  Workgroup i of
+// a stream takes the row groups i and G - 1 - i (G = row groups of the block) and deals its NR NS
+// wavefronts out between them in proportion to their key tiles (under the causal masks the
+// early rows see few keys and the late rows many).  Every wavefront then streams its share of
+// its group's tiles through a private K buffer and V buffer, one tile each (K refilled once
+// S is formed, V once P V is done), and each group's partial states are merged at the end.  The
+// longest sweep of a wavefront then follows the pair's work, not the heaviest row group's.
 template <int QB, int TK, bool STATS, int NR, int NS, int NST>
 struct Attn {
   static constexpr int NW = NR * NS;              // wavefronts per workgroup
@@ -89,9 +97,12 @@ struct Attn {
   static constexpr int TILE = TK * ROWB;          // bytes of one K or V tile
   static constexpr int SPLIT_BYTES = 2 * NST * TILE;              // K stages, then V stages
   static constexpr int SLOT = QB * (64 * 64 * 4 + 2 * 64 * 4);    // one wavefront's O, m, l
-  static constexpr int MERGE_BYTES = (NS - 1) * NR * SLOT;
-  static constexpr int LDS_BYTES = NS * SPLIT_BYTES > MERGE_BYTES ? NS * SPLIT_BYTES : MERGE_BYTES;
-  static_assert(NST == 2 || NST == 3, "two or three stages");
+  static constexpr bool PAIRED = NST == 1;
+  static constexpr int STAGE_BYTES = PAIRED ? NW * SPLIT_BYTES : NS * SPLIT_BYTES;
+  static constexpr int MERGE_BYTES = PAIRED ? NW * SLOT : (NS - 1) * NR * SLOT;
+  static constexpr int LDS_BYTES = STAGE_BYTES > MERGE_BYTES ? STAGE_BYTES : MERGE_BYTES;
+  static_assert(NST >= 1 && NST <= 3, "one (paired), two or three stages");
+  static_assert(!PAIRED || (NR == 2 && QB == 1), "paired mode: two row groups of 32 queries");
 
   // Per-lane constant parts of the LDS addresses (split base included).
   int k_base[8];       // K operand: row l32, chunk (2 dk + hh)
@@ -118,7 +129,9 @@ __global__ __launch_bounds__(NR * NS * 64, RA_BF16_OCC) void k_attn_bf16(AttnArg
   const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = NS == 1 ? wave_u : wave_u % NR;   // row group
   const int s = NS == 1 ? 0 : wave_u / NR;        // key split
-  const int split_base = s * A::SPLIT_BYTES;
+  constexpr bool PAIRED = A::PAIRED;
+  constexpr int DNR = PAIRED ? 1 : NR;            // wavefronts sharing one tile's DMA
+  const int split_base = (PAIRED ? wave_u : s) * A::SPLIT_BYTES;
   char* const sb = smem + split_base;             // this split's stages
   const int l32 = lane & 31;
   const int hh = lane >> 5;
@@ -153,16 +166,49 @@ __global__ __launch_bounds__(NR * NS * 64, RA_BF16_OCC) void k_attn_bf16(AttnArg
   const int dev = stream / a.BH;
   const int p = a.p_begin + dev;
   const int q_wg0 = qt * TQ;
-  const int q_wg_last = min(c, q_wg0 + TQ) - 1;
-  const int qw0 = q_wg0 + g * QW;
+  // paired mode: this wavefront's index within its group, the group's wavefront count and the
+  // group's first row
+  int pw_idx = 0, pw_k = 1, prow = 0;
+  if constexpr (PAIRED) {
+    const int G = (c + QW - 1) / QW;
+    const int rga = qt, rgb = G - 1 - qt;
+    const int ntk_all0 = (c + TK - 1) / TK;
+    auto group_tiles = [&](int rg) -> int {
+      const int last = min(c, rg * QW + QW) - 1;
+      int n = 0;
+      for (int rr = 0; rr < a.r_count; ++rr) {
+        const int mode = round_mode(a.layout, a.causal, p, ring_block(p, a.r_begin + rr, a.P));
+        const int delta = mode == MODE_STRICT ? 1 : 0;
+        if (mode == MODE_FULL) n += ntk_all0;
+        else if (mode != MODE_SKIP && last - delta >= 0) n += min(ntk_all0, (last - delta) / TK + 1);
+      }
+      return n;
+    };
+    // wavefronts of group a: the split whose longest share is shortest (ties: the more even one)
+    int ka = NW;
+    if (rgb != rga) {
+      const int na = group_tiles(rga), nb = group_tiles(rgb);
+      int best = 1 << 30;
+      for (int k = 1; k < NW; ++k) {
+        const int worst = max((na + k - 1) / k, (nb + NW - k - 1) / (NW - k));
+        if (worst < best || (worst == best && abs(2 * k - NW) < abs(2 * ka - NW))) { best = worst; ka = k; }
+      }
+    }
+    const bool in_a = wave_u < ka;
+    pw_idx = in_a ? wave_u : wave_u - ka;
+    pw_k = in_a ? ka : NW - ka;
+    prow = (in_a ? rga : rgb) * QW;
+  }
+  const int q_wg_last = PAIRED ? min(c, prow + QW) - 1 : min(c, q_wg0 + TQ) - 1;
+  const int qw0 = PAIRED ? prow : q_wg0 + g * QW;
   const int qw_last = min(c, qw0 + QW) - 1;  // < qw0 when the wave has no rows
   const bool wave_live = qw0 < c;
 
   A off;
   off.init_offsets(lane, split_base);
-  unsigned kdma[DmaShape<NR, TK>::PER_WAVE], vdma[DmaShape<NR, TK>::PER_WAVE];
-  dma_init<NR, TK>(kdma, SWZ_K, g, lane, a.row_step);
-  dma_init<NR, TK>(vdma, SWZ_V, g, lane, a.row_step);
+  unsigned kdma[DmaShape<DNR, TK>::PER_WAVE], vdma[DmaShape<DNR, TK>::PER_WAVE];
+  dma_init<DNR, TK>(kdma, SWZ_K, PAIRED ? 0 : g, lane, a.row_step);
+  dma_init<DNR, TK>(vdma, SWZ_V, PAIRED ? 0 : g, lane, a.row_step);
 
   // ---- Q columns (B operand): lane holds row qw0 + 32 qb + l32, head dims 16 dk + 8 hh .. +7
   const __bf16* qp = (const __bf16*)a.q + bh * a.q_bh_stride + dev * a.q_dev_stride;
@@ -190,7 +236,7 @@ __global__ __launch_bounds__(NR * NS * 64, RA_BF16_OCC) void k_attn_bf16(AttnArg
   // before the softmax lets their LDS latency pass under the exp work; all of them would need
   // more registers than the 3-waves-per-SIMD budget leaves.  The counting variant, which holds
   // more registers and is never timed, keeps the reads next to the MFMAs.
-  constexpr int VPRE = STATS ? 0 : RA_BF16_VPRE;
+  constexpr int VPRE = STATS ? 0 : (PAIRED ? 1 : RA_BF16_VPRE);
   // Small workgroups read V^T without the compiler's wait for every LDS DMA in flight (their own
   // waits cover the tile); measured faster for them and slower for the 12-wave workgroups.
   constexpr bool TR_NOWAIT = NW <= 8;
@@ -331,6 +377,7 @@ __global__ __launch_bounds__(NR * NS * 64, RA_BF16_OCC) void k_attn_bf16(AttnArg
   };
 
   const int ntk_all = (c + TK - 1) / TK;
+  int pbase = 0;                                  // paired mode: tiles of the group in earlier rounds
   // tiles of [0, n) that split s takes (s, s + NS, ...)
   auto split_count = [&](int n) -> int { return NS == 1 ? n : (n > s ? (n - s + NS - 1) / NS : 0); };
   // Loads per tile and wavefront (K and V) for the partial wait of a three-stage pipeline; every
@@ -386,7 +433,38 @@ __global__ __launch_bounds__(NR * NS * 64, RA_BF16_OCC) void k_attn_bf16(AttnArg
       }
     };
 
-    if constexpr (NS == 1 && NST == 2) {
+    if constexpr (PAIRED) {
+      // The group's tiles, numbered on from the earlier rounds, go to its pw_k wavefronts in
+      // turn: this wavefront takes t0, t0 + pw_k, ...  One K and one V buffer of its own: K(t+1)
+      // is fetched once S of t is formed, V(t+1) once P V of t is done.  K and V DMAs of a tile
+      // are issued in that order and complete in order, so waiting until at most VL loads are
+      // outstanding means the older of the two has landed.
+      constexpr int VL = DmaShape<1, TK>::PER_WAVE;
+      const int t0 = ((pw_idx - pbase) % pw_k + pw_k) % pw_k;
+      pbase += ntk;
+      const int cnt = t0 < ntk ? (ntk - t0 + pw_k - 1) / pw_k : 0;
+      if (cnt > 0) {
+        dma_issue<1, TK>(kdma, kblk, sb, t0 * TK, c, a.row_step, 0);
+        dma_issue<1, TK>(vdma, vblk, sb + TILE, t0 * TK, c, a.row_step, 0);
+        for (int i = 0; i < cnt; ++i) {
+          const int t = t0 + i * pw_k;
+          const bool more = i + 1 < cnt;
+          vm_wait<VL>();                              // K(t) landed
+          const int cls = tile_class(t);
+          if (cls) compute_s(smem, sA);
+          lgkm_wait0();                               // K reads returned: the buffer may refill
+          if (more) dma_issue<1, TK>(kdma, kblk, sb, (t + pw_k) * TK, c, a.row_step, 0);
+          if (more) vm_wait<VL>();                    // V(t) landed (K(t + pw_k) in flight)
+          else vm_wait<0>();
+          if (cls) {
+            if (cls >= 2) apply_mask(sA, t, cls == 2);
+            softmax_pv(sA, smem + TILE);
+          }
+          lgkm_wait0();                               // V reads returned
+          if (more) dma_issue<1, TK>(vdma, vblk, sb + TILE, (t + pw_k) * TK, c, a.row_step, 0);
+        }
+      }
+    } else if constexpr (NS == 1 && NST == 2) {
       // One split, two stages: tile t lives in stage t & 1; its DMA was issued one iteration
       // earlier.  The loop is unrolled by two so that the stage offsets are compile-time
       // immediates.
@@ -471,8 +549,11 @@ __global__ __launch_bounds__(NR * NS * 64, RA_BF16_OCC) void k_attn_bf16(AttnArg
         atomicAdd((unsigned long long*)&st->unmasked_pairs, (unsigned long long)(pairs + st_pairs_uniform));
         atomicAdd((unsigned long long*)&st->tiles_full, (unsigned long long)st_full);
         atomicAdd((unsigned long long*)&st->tiles_diag, (unsigned long long)st_diag);
-        atomicAdd((unsigned long long*)&st->tiles_skipped,
-                  (unsigned long long)(split_count(ntk_all) - st_full - st_diag));
+        // skipped tiles of a row group: all of them less those its wavefronts visited (in the
+        // paired mode the group's first wavefront adds the group's tiles, every one subtracts
+        // its own; the unsigned sum wraps to the group's count)
+        const uint64_t own = PAIRED ? (pw_idx == 0 ? (uint64_t)ntk_all : 0) : (uint64_t)split_count(ntk_all);
+        atomicAdd((unsigned long long*)&st->tiles_skipped, (unsigned long long)(own - st_full - st_diag));
       }
     }
   }
@@ -480,7 +561,47 @@ __global__ __launch_bounds__(NR * NS * 64, RA_BF16_OCC) void k_attn_bf16(AttnArg
   // ---- key splits: splits 1 .. NS-1 hand (m, l, O) to split 0 of their row group through LDS;
   // split 0 folds them in with the blockwise softmax merge (both sides rescaled to the larger
   // reference; a side that saw no key has m = -inf and contributes nothing).
-  if constexpr (NS > 1) {
+  if constexpr (PAIRED) {
+    // every wavefront parks (m, l, O) in its slot; the first wavefront of each group folds in
+    // the others of the group with the same merge rule
+    __syncthreads();                                  // every wavefront is done with its buffers
+    {
+      char* const slot = smem + wave_u * A::SLOT;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          reinterpret_cast<float4*>(slot)[(db * 4 + q4) * 64 + lane] =
+              make_float4(o[0][db][4 * q4], o[0][db][4 * q4 + 1], o[0][db][4 * q4 + 2], o[0][db][4 * q4 + 3]);
+      float* ml = reinterpret_cast<float*>(slot + 64 * 64 * 4);
+      ml[lane] = m[0];
+      ml[64 + lane] = l[0];
+    }
+    __syncthreads();
+    if (pw_idx != 0) return;
+#pragma unroll 1
+    for (int j = 1; j < pw_k; ++j) {
+      const char* const slot = smem + (wave_u + j) * A::SLOT;
+      const float* ml = reinterpret_cast<const float*>(slot + 64 * 64 * 4);
+      const float m2 = ml[lane], l2 = ml[64 + lane];
+      const float mn = fmaxf(m[0], m2);
+      const float al = m[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[0] - mn);
+      const float be = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
+      l[0] = al * l[0] + be * l2;
+      m[0] = mn;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 w = reinterpret_cast<const float4*>(slot)[(db * 4 + q4) * 64 + lane];
+          o[0][db][4 * q4] = al * o[0][db][4 * q4] + be * w.x;
+          o[0][db][4 * q4 + 1] = al * o[0][db][4 * q4 + 1] + be * w.y;
+          o[0][db][4 * q4 + 2] = al * o[0][db][4 * q4 + 2] + be * w.z;
+          o[0][db][4 * q4 + 3] = al * o[0][db][4 * q4 + 3] + be * w.w;
+        }
+    }
+  }
+  if constexpr (NS > 1 && !PAIRED) {
     __syncthreads();                                  // every split is done with its stages
     if (s > 0) {
       char* const slot = smem + ((s - 1) * NR + g) * A::SLOT;
@@ -588,16 +709,33 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// True when no round of the launch shows a row group every key: causal, and no contiguous round
+// with k < p (that is, with r mod P in 1..p for a launched device p).  Row groups then have work
+// that grows with their position in the block, which the paired workgroups balance.
+bool triangular_rounds(const AttnArgs& a) {
+  if (!a.causal) return false;
+  if (a.layout != RA_CONTIGUOUS) return true;
+  const int p_max = a.p_begin + a.n_dev - 1;
+  for (int i = 0; i < a.r_count && i < a.P; ++i) {
+    const int res = (a.r_begin + i) % a.P;
+    if (res >= 1 && res <= p_max) return false;
+  }
+  return true;
+}
+
 }  // namespace
 
 // Workgroup shape by grid size.  Wide workgroups (one per CU, 384 queries sharing each K/V tile)
 // when the grid has at least two of them per CU.  Below that, a round lasts about as long as the
 // longest sweep of one wavefront over its key tiles, and the smaller the grid the more that sweep
 // is split over wavefronts: with G = 32-row groups of the whole launch and C compute units,
+//   G <= 2 C and every round triangular (see triangular_rounds): the paired mode (8 wavefronts
+//               for two row groups, 132 KB LDS, the whole launch resident at once),
 //   G <= 4 C:   2 row groups x 4 key splits (8 wavefronts, 128 KB LDS, one workgroup per CU),
 //   G <= 12 C:  2 row groups x 2 key splits (4 wavefronts, 64 KB LDS, two per CU),
 //   otherwise:  4 row groups, one split, three LDS stages (4 wavefronts, 48 KB LDS).
-// The same shape serves both layouts: it depends on the grid, not on the mask.
+// Apart from the paired mode, which only pays when the row groups' work differs, the shape
+// depends on the grid, not on the mask.
 hipError_t launch_attn_bf16(const AttnArgs& a, int d, hipStream_t s) {
   if (d != D) return hipErrorInvalidValue;
   const int64_t cus = cu_count();
@@ -605,6 +743,7 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int d, hipStream_t s) {
   const int64_t wide = (int64_t)((a.c + TQW - 1) / TQW) * a.BH * a.n_dev;
   if (wide >= 2 * cus) return launch_cfg<RA_BF16_NW, 1, 2>(a, s);
   const int64_t groups = (int64_t)((a.c + 32 * QB_SEL - 1) / (32 * QB_SEL)) * a.BH * a.n_dev;
+  if (groups <= 2 * cus && triangular_rounds(a)) return launch_cfg<2, 4, 1>(a, s);
   if (groups <= 4 * cus) return launch_cfg<2, 4, 2>(a, s);
   if (groups <= 12 * cus) return launch_cfg<2, 2, 2>(a, s);
   return launch_cfg<4, 1, 3>(a, s);

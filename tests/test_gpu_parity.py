@@ -389,10 +389,12 @@ def test_wide_workgroup_path(ra, layout):
 def test_small_grid_workgroup_shapes(ra, H, P, c):
     """Grids below two 12-wave workgroups per CU pick their workgroup shape by the number of
     32-row groups G in the launch; on a 256-CU device these three cases take 2 row groups x 4 key
-    splits (G = 256), 2 x 2 (G = 2432) and 4 row groups with three LDS stages (G = 4224), all
-    with a ragged last tile.  The split workgroups merge their partial softmax states in LDS;
-    element-wise against the oracle on three heads, counters on all, and one round per direction
-    (whose single-device grids take the split shapes too)."""
+    splits (G = 256; the striped launches and the contiguous diagonal round, whose row groups'
+    work grows with their position, take the paired mode instead), 2 x 2 (G = 2432) and 4 row
+    groups with three LDS stages (G = 4224), all with a ragged last tile.  The split workgroups merge their partial softmax states in LDS;
+    element-wise against the oracle on three heads, counters on all, token-order tensors
+    bit-identical to the permuted path, and one round per direction (whose single-device grids
+    take the split shapes too)."""
     B, d = 1, 128
     n = P * c
     g = torch.Generator().manual_seed(4100 + H + c)
@@ -410,7 +412,13 @@ def test_small_grid_workgroup_shapes(ra, H, P, c):
         idx = torch.tensor(heads, device="cuda")
         compare(o.index_select(1, idx), lse.index_select(1, idx), o_ref, l_ref, "bf16", f"H={H} c={c} {layout}")
         assert np.array_equal(stats.cpu().numpy(), _expected_stats(layout, P, c, B * H, True, tq, tk))
-        for p, kk in ((P - 1, 0), (0, P - 1)):
+        if layout == "striped":
+            # token-order tensors (rows P apart in every tile) take the same shape: bit-identical
+            o_t, l_t = ra.forward(q.cuda(), k.cuda(), v.cuda(), P, "striped_tokens", True, o_dtype=torch.float32)
+            torch.cuda.synchronize()
+            assert torch.equal(o_t, ra.permute(o, P, inverse=True))
+            assert torch.equal(l_t, ra.permute(lse, P, dim=-1, inverse=True))
+        for p, kk in ((P - 1, 0), (0, P - 1), (P - 1, P - 1)):
             po, pl = ra.round(qg[:, :, p * c:(p + 1) * c], kg[:, :, kk * c:(kk + 1) * c], vg[:, :, kk * c:(kk + 1) * c],
                               P, p, kk, layout, True)
             torch.cuda.synchronize()
