@@ -81,9 +81,10 @@ constexpr float LAZY_LIM = 4096.0f;   // 2^(TAU + 4)
 // tiles in flight while one computes.
 //
 // NST = 1 is the paired mode, for launches small enough to be resident at once.  Workgroup i of
-// a stream takes the row groups i and G - 1 - i (G = row groups of the block) and deals its NR NS
-// wavefronts out between them in proportion to their key tiles (under the causal masks the
-// early rows see few keys and the late rows many).  Every wavefront then streams its share of
+// a stream takes the row groups i and G - 1 - i (G = row groups of the block) and divides its
+// NR NS wavefronts between them so that the longer of the two groups' per-wavefront shares of
+// key tiles is as short as it can be (under the causal masks the early rows see few keys and
+// the late rows many).  Every wavefront then streams its share of
 // its group's tiles through a private K buffer and V buffer, one tile each (K refilled once
 // S is formed, V once P V is done), and each group's partial states are merged at the end.  The
 // longest sweep of a wavefront then follows the pair's work, not the heaviest row group's.
@@ -235,7 +236,9 @@ __global__ __launch_bounds__(NR * NS * 64, RA_BF16_OCC) void k_attn_bf16(AttnArg
   // When the V^T fragments are read (see RA_BF16_VPRE).  Reading the first 16 keys' fragments
   // before the softmax lets their LDS latency pass under the exp work; all of them would need
   // more registers than the 3-waves-per-SIMD budget leaves.  The counting variant, which holds
-  // more registers and is never timed, keeps the reads next to the MFMAs.
+  // more registers and is never timed, keeps the reads next to the MFMAs.  The paired mode
+  // reads them all after the softmax, so that the single V buffer's next fill has the S and
+  // softmax phases to land in.
   constexpr int VPRE = STATS ? 0 : (PAIRED ? 1 : RA_BF16_VPRE);
   // Small workgroups read V^T without the compiler's wait for every LDS DMA in flight (their own
   // waits cover the tile); measured faster for them and slower for the 12-wave workgroups.
