@@ -87,14 +87,19 @@ def test_token_order_seq8k_bf16(ra):
         assert torch.equal(o, o_p) and torch.equal(lse, l_p)
 
 
-def test_token_order_not_causal(ra):
-    P, c, H = 4, 100, 2
-    g = torch.Generator().manual_seed(77)
+@pytest.mark.parametrize("P,c", [(4, 100), (64, 1)])
+def test_token_order_not_causal(ra, P, c):
+    """Unmasked rounds in token order.  With P = 64 and c = 1 every round has one key tile, so
+    three of the four key splits of the small-grid workgroups own none while their rows lie 64
+    tokens apart: a split must not fetch a tile it does not own (it would start past the
+    block)."""
+    H = 2
+    g = torch.Generator().manual_seed(77 + P)
     q, k, v = (torch.randn((1, H, P * c, 128), generator=g).to(torch.bfloat16) for _ in range(3))
     o_ref, l_ref = OA.attention(q, k, v, False)
     o, lse = ra.forward(q.cuda(), k.cuda(), v.cuda(), P, "striped_tokens", False, o_dtype=torch.float32)
     torch.cuda.synchronize()
-    compare(o, lse, o_ref, l_ref, "bf16", "token order, no mask")
+    compare(o, lse, o_ref, l_ref, "bf16", f"token order, no mask, P={P} c={c}")
 
 
 @pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64)])
