@@ -76,13 +76,16 @@ def source_hash(paths) -> str:
     return h.hexdigest()
 
 
-def traffic_from_profile(launch_bytes_hint=None):
+def traffic_from_profile(workload: str):
     """HBM bytes per launch of the fused forward from committed rocprofv3 --pmc counters, or
-    None when the counters are missing or were taken on a different kernel source."""
+    None when the counters are missing, were taken on another workload or on a different
+    kernel source."""
     try:
         with open(PMC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
+        return None
+    if rec.get("workload_name") != workload:
         return None
     if rec.get("kernel_source_sha256") != source_hash(KERNEL_SRCS):
         return None
@@ -404,7 +407,7 @@ def main(argv=None) -> int:
         "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 3),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 5),
-                     "traffic": traffic_from_profile(), "kernel": "k_attn_bf16 (ra_forward)",
+                     "traffic": traffic_from_profile(w.name), "kernel": "k_attn_bf16 (ra_forward)",
                      "kernel_ms": round(fwd_avg, 4), "algorithmic_flops_per_launch": flops_s},
         "wall_s_timed": round(wall, 3),
     }
