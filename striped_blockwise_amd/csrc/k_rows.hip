@@ -12,6 +12,9 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 #ifndef RA_ROWS_NT
 #define RA_ROWS_NT 1            // 1: streamed loads and stores marked non-temporal (merge, delta, RoPE)
 #endif
+#ifndef RA_MERGE_ROWS
+#define RA_MERGE_ROWS 4         // merge rows in flight per lane group for d = 64 and 128 (1: generic kernel)
+#endif
 // Every byte these kernels move is touched once, so marking the accesses non-temporal keeps
 // them from displacing useful lines in the caches.
 template <typename V>
@@ -154,6 +157,58 @@ __global__ __launch_bounds__(256) void k_merge(float* __restrict__ o_acc, float*
       for (int64_t j = li; j < d; j += LPR) oa[j] = wa * oa[j] + wb * ob[j];
     }
     if (li == 0) lse_acc[row] = L;
+  }
+}
+
+// The same merge for rows of exactly LPR float4s (d = 4 LPR, LPR a power of two <= 64): each
+// lane owns one float4 of a row, and the loads of U row groups (both LSEs, both O slices) are
+// all issued before any of them is used, so that U times more reads are in flight per lane.
+template <int LPR, int U>
+__global__ __launch_bounds__(256) void k_merge_v4(float* __restrict__ o_acc, float* __restrict__ lse_acc,
+                                                  const float* __restrict__ o_part,
+                                                  const float* __restrict__ lse_part, int64_t rows) {
+  constexpr int RPW = 64 / LPR;                           // rows per wavefront and group
+  constexpr int D = 4 * LPR;
+  const int lane = threadIdx.x & 63;
+  const int sub = lane / LPR;
+  const int li = lane % LPR;
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  for (int64_t base = wave * (RPW * U); base < rows; base += nwaves * (RPW * U)) {
+    float la[U], lb[U];
+    f32x4v a[U], b[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t row = base + u * RPW + sub;
+      la[u] = lb[u] = -INFINITY;
+      a[u] = b[u] = f32x4v{};
+      if (row < rows) {
+        la[u] = lse_acc[row];
+        lb[u] = lse_part[row];
+        a[u] = ld_stream(reinterpret_cast<const f32x4v*>(o_acc + row * D) + li);
+        b[u] = ld_stream(reinterpret_cast<const f32x4v*>(o_part + row * D) + li);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t row = base + u * RPW + sub;
+      if (row >= rows) continue;
+      const float mx = fmaxf(la[u], lb[u]);
+      float wa = 0.f, wb = 0.f, L = -INFINITY;
+      if (mx != -INFINITY) {
+        const float ea = expf(la[u] - mx);
+        const float eb = expf(lb[u] - mx);
+        const float sum = ea + eb;
+        L = mx + logf(sum);
+        wa = ea / sum;
+        wb = eb / sum;
+      }
+      f32x4v r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = wa * a[u][e] + wb * b[u][e];
+      st_stream(r, reinterpret_cast<f32x4v*>(o_acc + row * D) + li);
+      if (li == 0) lse_acc[row] = L;
+    }
   }
 }
 
@@ -400,6 +455,17 @@ hipError_t launch_permute(const void* src, void* dst, int64_t BH, int64_t n, int
 
 hipError_t launch_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
                         int64_t rows, int64_t d, hipStream_t s) {
+  constexpr int U = RA_MERGE_ROWS;
+  if (U > 1 && (d == 128 || d == 64)) {
+    const int lpr = (int)(d / 4);
+    const uint64_t waves = (uint64_t)((rows + (64 / lpr) * U - 1) / ((64 / lpr) * U));
+    const int grid = grid_for(waves * 64, 256);
+    if (lpr == 32)
+      hipLaunchKernelGGL((k_merge_v4<32, U>), dim3(grid), dim3(256), 0, s, o_acc, lse_acc, o_part, lse_part, rows);
+    else
+      hipLaunchKernelGGL((k_merge_v4<16, U>), dim3(grid), dim3(256), 0, s, o_acc, lse_acc, o_part, lse_part, rows);
+    return hipGetLastError();
+  }
   const int64_t lanes_needed = (d % 4 == 0) ? d / 4 : d;
   int lpr = 1;
   while (lpr < lanes_needed && lpr < 64) lpr <<= 1;
