@@ -52,6 +52,82 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+class ClockSampler:
+    """Graphics clock and socket power of the GPU, sampled from the driver's metrics table
+    (amdsmi) in a host thread while a timed region runs.  Best effort: ``result()`` is None
+    when amdsmi is missing or refuses access."""
+
+    def __init__(self, torch, dev, period_s: float = 0.01):
+        import threading
+        self.samples = []
+        self.period = period_s
+        self.stop_ev = threading.Event()
+        self.thread = None
+        self.handle = None
+        self.err = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self.smi = amdsmi
+            handles = amdsmi.amdsmi_get_processor_handles()
+            bus = getattr(torch.cuda.get_device_properties(dev), "pci_bus_id", None)
+            for h in handles:
+                try:
+                    bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
+                    if bus is not None and int(bdf.split(":")[1], 16) == int(bus):
+                        self.handle = h
+                        break
+                except Exception:
+                    continue
+            if self.handle is None and len(handles) == 1:
+                self.handle = handles[0]
+        except Exception as e:  # pragma: no cover - depends on the box
+            self.err = repr(e)
+
+    def _read(self):
+        m = self.smi.amdsmi_get_gpu_metrics_info(self.handle)
+        clks = [x for x in (m.get("current_gfxclks") or []) if isinstance(x, (int, float)) and 0 < x < 10000]
+        clk = sum(clks) / len(clks) if clks else m.get("current_gfxclk")
+        pw = m.get("current_socket_power")
+        if not isinstance(pw, (int, float)) or pw <= 0 or pw > 100000:
+            pw = m.get("average_socket_power")
+        return clk, pw
+
+    def _run(self):
+        while not self.stop_ev.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception as e:  # pragma: no cover
+                self.err = repr(e)
+                return
+            self.stop_ev.wait(self.period)
+
+    def start(self):
+        import threading
+        if self.handle is None:
+            return self
+        self.thread = threading.Thread(target=self._run, daemon=True)
+        self.thread.start()
+        return self
+
+    def stop(self):
+        if self.thread is not None:
+            self.stop_ev.set()
+            self.thread.join()
+        return self
+
+    def result(self, cus: int):
+        clk = [c for c, _ in self.samples if isinstance(c, (int, float)) and 0 < c < 10000]
+        pw = [p for _, p in self.samples if isinstance(p, (int, float)) and 0 < p < 100000]
+        if not clk:
+            return None if self.err is None else {"error": self.err}
+        mhz = sum(clk) / len(clk)
+        return {"sclk_mhz_mean": round(mhz, 1), "samples": len(clk),
+                "socket_power_w_mean": round(sum(pw) / len(pw), 1) if pw else None,
+                "peak_at_sclk_tflops": round(cus * mhz * 1e6 * 4096 / 1e12, 1),
+                "source": "amdsmi gpu_metrics current_gfxclk(s), sampled every 10 ms over the timed region"}
+
+
 def useful_pairs(layout: str, P: int, c: int, p: int, causal: bool = True) -> list:
     """Unmasked pairs of device p per ring round (closed form of the Striped Attention review's
     work formulas, with the diagonal block's c(c+1)/2)."""
@@ -146,7 +222,6 @@ def per_round_all_devices(torch, ra, dev, name: str = "seq_n8k", reps: int = 5):
     import statistics
 
     import workloads
-    from oracle import ring as OR
     w = workloads.get(name)
     P, c = w.P, w.c
     q, k, v = (t.to(dev) for t in workloads.qkv(w))
@@ -161,7 +236,7 @@ def per_round_all_devices(torch, ra, dev, name: str = "seq_n8k", reps: int = 5):
         for r in range(P):
             per_dev = []
             for p in range(P):
-                kb = OR.kv_block(p, r, P)
+                kb = (p - r) % P                            # ring schedule: block of device p - r
                 args_r = (qq[:, :, p * c:(p + 1) * c], kk[:, :, kb * c:(kb + 1) * c], vv[:, :, kb * c:(kb + 1) * c],
                           P, p, kb, layout, True)
                 ts = []
@@ -177,8 +252,8 @@ def per_round_all_devices(torch, ra, dev, name: str = "seq_n8k", reps: int = 5):
         res[layout] = tmax
     ideal = []
     for r in range(P):
-        pc = max(OR.work_closed_form("contiguous", p, OR.kv_block(p, r, P), c, True) for p in range(P))
-        ps = max(OR.work_closed_form("striped", p, OR.kv_block(p, r, P), c, True) for p in range(P))
+        pc = max(useful_pairs("contiguous", P, c, p)[r] for p in range(P))
+        ps = max(useful_pairs("striped", P, c, p)[r] for p in range(P))
         ideal.append(round(pc / ps, 5))
     del flush, lay, q, k, v
     return {"workload": name, "n": w.n, "P": P, "H": w.H, "reps": reps,
@@ -288,6 +363,67 @@ def backward_leg(torch, ra, w, striped_qkv, contiguous_qkv, flops_s, flops_c, p,
     return out
 
 
+def stress_leg(torch, ra, dev, name: str = "stress_n1m", reps: int = 5):
+    """The million-token stress share (device 31 of P = 32, H = 8, 1% of key rows x8): the fused
+    striped forward on token-order tensors, and the streamed form (32 x ra_round + ra_merge on
+    the permuted blocks)."""
+    import workloads
+    w = workloads.get(name)
+    P, c, d, H, B = w.P, w.c, w.d, w.H, w.B
+    p = w.device if w.device is not None else P - 1
+    log(f"[bench] generating inputs for {w.name} (n={w.n}, P={P}, H={H}) on the CPU")
+    q, k, v = (t.to(dev) for t in workloads.qkv(w))
+    flops = 4.0 * d * B * H * sum(useful_pairs("striped", P, c, p))
+    o_t = torch.empty((B, H, w.n, d), dtype=torch.bfloat16, device=dev)
+    lse_t = torch.empty((B, H, w.n), dtype=torch.float32, device=dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fwd = lambda: ra.forward(q, k, v, P, "striped_tokens", True, p_begin=p, p_end=p + 1, out=(o_t, lse_t))
+    fwd()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a.record()
+        fwd()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    ts.sort()
+    f_ms = ts[len(ts) // 2]
+    qs, ks, vs = (ra.permute(t, P) for t in (q, k, v))
+    del q, k, v, o_t, lse_t
+    po = torch.empty((B, H, c, d), dtype=torch.float32, device=dev)
+    pl = torch.empty((B, H, c), dtype=torch.float32, device=dev)
+    acc_o, acc_l = torch.empty_like(po), torch.empty_like(pl)
+
+    def streamed():
+        acc_o.zero_()
+        acc_l.fill_(float("-inf"))
+        for r in range(P):
+            kb = (p - r) % P
+            ra.round(qs[:, :, p * c:(p + 1) * c], ks[:, :, kb * c:(kb + 1) * c], vs[:, :, kb * c:(kb + 1) * c],
+                     P, p, kb, "striped", True, out=(po, pl))
+            ra.merge(acc_o, acc_l, po, pl)
+
+    streamed()
+    torch.cuda.synchronize()
+    a.record()
+    streamed()
+    b.record()
+    torch.cuda.synchronize()
+    s_ms = a.elapsed_time(b)
+    del qs, ks, vs, po, pl, acc_o, acc_l
+    torch.cuda.empty_cache()
+    out = {"workload": name, "n": w.n, "P": P, "c": c, "device": p, "H": H, "useful_flops": flops,
+           "forward_ms": round(f_ms, 4), "forward_tflops": round(flops / (f_ms * 1e-3) / 1e12, 3),
+           "forward_pct_peak": round(100 * flops / (f_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 3),
+           "forward_timing": f"median of {reps}, ra_forward RA_STRIPED_TOKENS",
+           "streamed_ms": round(s_ms, 4), "streamed_tflops": round(flops / (s_ms * 1e-3) / 1e12, 3),
+           "streamed": "32 x (ra_round + ra_merge) on ra_permute'd blocks, one timed pass"}
+    log(f"[bench] {name}: fused forward {f_ms:.2f} ms ({out['forward_tflops']:.1f} TFLOP/s); "
+        f"streamed {s_ms:.2f} ms")
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -378,7 +514,9 @@ def main(argv=None) -> int:
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sampler = ClockSampler(torch, dev)
     torch.cuda.synchronize()
+    sampler.start()
     wall0 = time.perf_counter()
     s0.record()
     for i in range(args.steps):
@@ -387,17 +525,26 @@ def main(argv=None) -> int:
     s1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    step_ms = s0.elapsed_time(s1) / args.steps
-    fwd_ms = [a.elapsed_time(b) for a, b in ev]
+    sampler.stop()
+    step_mean = s0.elapsed_time(s1) / args.steps
+    # the step is the one forward launch: its per-step event times, median over the K steps
+    fwd_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    step_ms = fwd_ms[len(fwd_ms) // 2] if len(fwd_ms) % 2 else 0.5 * (fwd_ms[len(fwd_ms) // 2 - 1] + fwd_ms[len(fwd_ms) // 2])
     fwd_avg = sum(fwd_ms) / len(fwd_ms)
     value = flops_s / (step_ms * 1e-3) / 1e12
     achieved = flops_s / (fwd_avg * 1e-3) / 1e12
-    log(f"[bench] striped step {step_ms:.2f} ms ({value:.1f} TFLOP/s); forward kernel {fwd_avg:.2f} ms "
-        f"({achieved:.1f} TFLOP/s, {100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    clock = sampler.result(cus)
+    log(f"[bench] striped step median {step_ms:.2f} ms ({value:.1f} TFLOP/s), mean {step_mean:.2f} ms; forward "
+        f"kernel mean {fwd_avg:.2f} ms ({achieved:.1f} TFLOP/s, {100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
+    if clock and "sclk_mhz_mean" in clock:
+        log(f"[bench] sclk {clock['sclk_mhz_mean']:.0f} MHz, socket power {clock['socket_power_w_mean']} W: "
+            f"peak at that clock {clock['peak_at_sclk_tflops']:.0f} TFLOP/s")
 
     result = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "ms_per_step_mean": round(step_mean, 4), "step_time": "median of the K steps' own HIP-event times",
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1)*0.5 bf16 Q/K/V, generated on the host)",
         "config": {"workload": w.name, "n": w.n, "P": P, "c": c, "device": p, "B": B, "H": H, "d": d,
@@ -408,7 +555,10 @@ def main(argv=None) -> int:
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 5),
                      "traffic": traffic_from_profile(w.name), "kernel": "k_attn_bf16 (ra_forward)",
-                     "kernel_ms": round(fwd_avg, 4), "algorithmic_flops_per_launch": flops_s},
+                     "kernel_ms": round(fwd_avg, 4), "algorithmic_flops_per_launch": flops_s,
+                     "clock": clock,
+                     "frac_of_peak_at_sclk": (round(achieved / clock["peak_at_sclk_tflops"], 5)
+                                              if clock and clock.get("peak_at_sclk_tflops") else None)},
         "wall_s_timed": round(wall, 3),
     }
 
@@ -500,7 +650,20 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         stream_ms = a.elapsed_time(b)
         merge_bytes = 3.0 * BH * c * (4 * d + 4)
-        mavg = sum(merge_ms) / len(merge_ms)
+        # merge bandwidth on its own: a 512 MB write before each timed merge, so that neither
+        # operand is still in the 256 MB Infinity Cache from the round that produced it
+        flush = torch.empty(128 * 2 ** 20, dtype=torch.float32, device=dev)
+        merge_ms = []
+        for _ in range(5):
+            flush.fill_(1.0)
+            m0.record()
+            ra.merge(acc_o, acc_l, po, pl)
+            m1.record()
+            torch.cuda.synchronize()
+            merge_ms.append(m0.elapsed_time(m1))
+        del flush
+        merge_ms.sort()
+        mavg = merge_ms[len(merge_ms) // 2]
         # permute bandwidth
         a.record()
         for _ in range(3):
@@ -521,7 +684,7 @@ def main(argv=None) -> int:
         result["streamed"] = {"rounds_plus_merges_ms": round(stream_ms, 3),
                               "tflops": round(flops_s / (stream_ms * 1e-3) / 1e12, 3)}
         result["hbm_kernels"] = {
-            "merge": {"ms": round(mavg, 4), "bytes": merge_bytes,
+            "merge": {"ms": round(mavg, 4), "bytes": merge_bytes, "timing": "median of 5, cache flushed before each",
                       "GBps": round(merge_bytes / (mavg * 1e-3) / 1e9, 1), "peak_GBps": PEAK_HBM_GBS},
             "permute": {"ms": round(perm_ms, 4), "bytes": perm_bytes,
                         "GBps": round(perm_bytes / (perm_ms * 1e-3) / 1e9, 1), "peak_GBps": PEAK_HBM_GBS},
@@ -538,6 +701,9 @@ def main(argv=None) -> int:
         result["per_round_all_devices"] = per_round_all_devices(torch, ra, dev)
         log("[bench] seq_n8k per-round speedup (slowest device) "
             + " ".join(f"{x:.3f}" for x in result["per_round_all_devices"]["speedup_striped_over_ring"]))
+
+    if not args.no_extras and w.name != "stress_n1m":
+        result["stress_n1m"] = stress_leg(torch, ra, dev)
 
     if not args.no_extras:
         # context: a plain library GEMM (torch.matmul -> hipBLASLt), bf16, square 8192, on the

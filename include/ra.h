@@ -36,6 +36,9 @@
  *     was launched.  ra_last_error() then holds a message (per calling thread).  A failed
  *     launch returns RA_E_HIP.  No C++ exception or abort crosses the ABI.
  *   - An empty problem (B, H or n equal to 0) is valid and enqueues nothing.
+ *   - No kernel loops on data values, so any input (NaN and infinities included) ends.  A NaN
+ *     input reaches the outputs of the rows that use it; a NaN in V can also reach the O rows
+ *     of the 32 x 32 tiles that mask it (0 x NaN in a matrix product), and no other row.
  */
 #ifndef RA_H_
 #define RA_H_
@@ -46,7 +49,7 @@
 extern "C" {
 #endif
 
-#define RA_ABI_VERSION 4
+#define RA_ABI_VERSION 5
 
 typedef int32_t ra_status_t;
 enum {
@@ -156,7 +159,8 @@ ra_status_t ra_permute_rope(const void* src, void* dst, const int64_t* pos, int6
  *   lse_part: [B, H, c] float32: log-sum-exp of those scores
  * A query row with no visible key in this block (striped later-device row 0, or a contiguous
  * block from a later device) gets o_part = 0 and lse_part = -inf, the identity of ra_merge.
- * stats: NULL, or one device-memory ra_round_stats_t that the call adds its counts to. */
+ * stats: NULL, or one device-memory ra_round_stats_t that the call adds its counts to.
+ * Outputs (o_part, lse_part, stats) must not overlap q, k, v or each other (RA_E_INVAL). */
 ra_status_t ra_round(const ra_problem_t* prob, const void* q, const void* k, const void* v,
                      int64_t q_stride_bh, int64_t kv_stride_bh, int32_t p, int32_t kv,
                      float* o_part, float* lse_part, ra_round_stats_t* stats, void* stream);
@@ -165,7 +169,8 @@ ra_status_t ra_round(const ra_problem_t* prob, const void* q, const void* k, con
  * Sequence Parallelism": per-node denominators add):
  *   L = ln(e^{lse_acc} + e^{lse_part}),  o_acc = e^{lse_acc - L} o_acc + e^{lse_part - L} o_part,
  *   lse_acc = L, for `rows` rows of d float32 values (o arrays contiguous [rows, d]).
- * Rows where both sides are -inf stay (0, -inf).  Start an accumulation from o_acc = 0,
+ * Rows where both sides are -inf stay (0, -inf); a NaN LSE on either side gives NaN O and LSE.
+ * Start an accumulation from o_acc = 0,
  * lse_acc = -inf (or copy the first partial).  o_part/lse_part must not alias the acc. */
 ra_status_t ra_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
                      int64_t rows, int64_t d, void* stream);
@@ -180,8 +185,10 @@ ra_status_t ra_merge(float* o_acc, float* lse_acc, const float* o_part, const fl
  *        [B, H, n]; only the rows of the selected devices (tokens t with p_begin <= t mod P
  *        < p_end) are written, so the range 0..P gives causal attention over the sequence with
  *        no permutation pass before or after
- *   stats: NULL or device memory [P][P] ra_round_stats_t indexed [p][r]; counts are added
- *          (zero it first); only rows p_begin..p_end-1 are touched. */
+ *   stats: NULL or device memory [P][P] ra_round_stats_t indexed [p][r]; the call clears rows
+ *          p_begin..p_end-1 on the stream and writes their counts there; other rows are not
+ *          touched.
+ * Outputs (o, lse, stats) must not overlap q, k, v or each other (RA_E_INVAL). */
 ra_status_t ra_forward(const ra_problem_t* prob, const void* q, const void* k, const void* v,
                        int32_t p_begin, int32_t p_end, void* o, int32_t o_dtype, float* lse,
                        ra_round_stats_t* stats, void* stream);

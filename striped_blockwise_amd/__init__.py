@@ -271,7 +271,8 @@ def forward(q, k, v, P: int, layout="contiguous", causal=True, p_begin: int = 0,
 
     q, k, v: contiguous [B, H, n, d] in layout order.  Returns (o, lse): o is
     [B, H, (p_end-p_begin)*c, d] in o_dtype (default: q's dtype), lse the matching float32
-    log-sum-exp (None if want_lse is False).  stats: None or new_stats(P).
+    log-sum-exp (None if want_lse is False).  stats: None or new_stats(P); the call clears the rows
+    p_begin..p_end-1 of it on the stream and writes their counts there.
     layout "striped_tokens": q, k, v, o and lse in token order, o [B, H, n, d] and lse [B, H, n];
     rows of devices outside the range are left as they were (zeros when out is None).
     out: None or (o, lse) of those shapes, contiguous (lse may be None).

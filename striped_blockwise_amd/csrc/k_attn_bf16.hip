@@ -175,26 +175,10 @@ __global__ __launch_bounds__(NR * NS * 64, RA_BF16_OCC) void k_attn_bf16(AttnArg
     const int rga = qt, rgb = G - 1 - qt;
     const int ntk_all0 = (c + TK - 1) / TK;
     auto group_tiles = [&](int rg) -> int {
-      const int last = min(c, rg * QW + QW) - 1;
-      int n = 0;
-      for (int rr = 0; rr < a.r_count; ++rr) {
-        const int mode = round_mode(a.layout, a.causal, p, ring_block(p, a.r_begin + rr, a.P));
-        const int delta = mode == MODE_STRICT ? 1 : 0;
-        if (mode == MODE_FULL) n += ntk_all0;
-        else if (mode != MODE_SKIP && last - delta >= 0) n += min(ntk_all0, (last - delta) / TK + 1);
-      }
-      return n;
+      return rounds_tiles(a.layout, a.causal, p, a.P, a.r_begin, a.r_count, min(c, rg * QW + QW) - 1, ntk_all0, TK);
     };
     // wavefronts of group a: the split whose longest share is shortest (ties: the more even one)
-    int ka = NW;
-    if (rgb != rga) {
-      const int na = group_tiles(rga), nb = group_tiles(rgb);
-      int best = 1 << 30;
-      for (int k = 1; k < NW; ++k) {
-        const int worst = max((na + k - 1) / k, (nb + NW - k - 1) / (NW - k));
-        if (worst < best || (worst == best && abs(2 * k - NW) < abs(2 * ka - NW))) { best = worst; ka = k; }
-      }
-    }
+    const int ka = rgb != rga ? paired_split(group_tiles(rga), group_tiles(rgb), NW, false) : NW;
     const bool in_a = wave_u < ka;
     pw_idx = in_a ? wave_u : wave_u - ka;
     pw_k = in_a ? ka : NW - ka;
@@ -382,7 +366,7 @@ __global__ __launch_bounds__(NR * NS * 64, RA_BF16_OCC) void k_attn_bf16(AttnArg
   const int ntk_all = (c + TK - 1) / TK;
   int pbase = 0;                                  // paired mode: tiles of the group in earlier rounds
   // tiles of [0, n) that split s takes (s, s + NS, ...)
-  auto split_count = [&](int n) -> int { return NS == 1 ? n : (n > s ? (n - s + NS - 1) / NS : 0); };
+  auto my_tiles = [&](int n) -> int { return NS == 1 ? n : split_count(n, s, NS); };
   // Loads per tile and wavefront (K and V) for the partial wait of a three-stage pipeline; every
   // wavefront of a split then issues the same number.
   constexpr int LPT = 2 * DmaShape<NR, TK>::PER_WAVE;
@@ -393,9 +377,7 @@ __global__ __launch_bounds__(NR * NS * 64, RA_BF16_OCC) void k_attn_bf16(AttnArg
     const int mode = round_mode(a.layout, a.causal, p, k);
     const int delta = mode == MODE_STRICT ? 1 : 0;
     // tiles this workgroup visits: up to the last one with a visible pair for its rows
-    int ntk = ntk_all;
-    if (mode == MODE_SKIP) ntk = 0;
-    else if (mode != MODE_FULL) ntk = (q_wg_last - delta < 0) ? 0 : min(ntk_all, (q_wg_last - delta) / TK + 1);
+    const int ntk = visited_tiles(mode, q_wg_last, ntk_all, TK);
 
     const int64_t kvo = bh * a.kv_bh_stride + (int64_t)(k - a.kv_base) * a.kv_blk_stride;
     const char* kblk = (const char*)((const __bf16*)a.k + kvo);
@@ -443,9 +425,9 @@ __global__ __launch_bounds__(NR * NS * 64, RA_BF16_OCC) void k_attn_bf16(AttnArg
       // are issued in that order and complete in order, so waiting until at most VL loads are
       // outstanding means the older of the two has landed.
       constexpr int VL = DmaShape<1, TK>::PER_WAVE;
-      const int t0 = ((pw_idx - pbase) % pw_k + pw_k) % pw_k;
+      int t0, cnt;
+      paired_deal(pw_idx, pw_k, pbase, ntk, t0, cnt);
       pbase += ntk;
-      const int cnt = t0 < ntk ? (ntk - t0 + pw_k - 1) / pw_k : 0;
       if (cnt > 0) {
         dma_issue<1, TK>(kdma, kblk, sb, t0 * TK, c, a.row_step, 0);
         dma_issue<1, TK>(vdma, vblk, sb + TILE, t0 * TK, c, a.row_step, 0);
@@ -500,13 +482,13 @@ __global__ __launch_bounds__(NR * NS * 64, RA_BF16_OCC) void k_attn_bf16(AttnArg
     } else {
       // This split's tiles: j = 0 .. my_n - 1 is tile j NS + s.  Wavefronts that share tiles
       // (NR > 1) run the same iteration count in lock-step; a lone wavefront runs its own.
-      const int my_n = split_count(ntk);
+      const int my_n = my_tiles(ntk);
       const int nit = NR > 1 ? (ntk + NS - 1) / NS : my_n;
       if (nit > 0) {
         // my tile j lives in stage j % NST; its DMA was issued NST - 1 iterations earlier.  The
         // loop is unrolled by NST so that the stage offsets are compile-time immediates.
         auto issue = [&](int j, int stage) __attribute__((always_inline)) {
-          const int x0 = (j * NS + s) * TK;
+          const int x0 = split_tile(j, s, NS) * TK;
           dma_issue<NR, TK>(kdma, kblk, sb + stage * TILE, x0, c, a.row_step, g);
           dma_issue<NR, TK>(vdma, vblk, sb + (NST + stage) * TILE, x0, c, a.row_step, g);
         };
@@ -523,7 +505,7 @@ __global__ __launch_bounds__(NR * NS * 64, RA_BF16_OCC) void k_attn_bf16(AttnArg
           if (NR > 1) __syncthreads();
           if (j + NST - 1 < my_n) issue(j + NST - 1, (S + NST - 1) % NST);
           if (NR == 1 || j < my_n) {
-            const int t = j * NS + s;
+            const int t = split_tile(j, s, NS);
             const int cls = tile_class(t);
             if (cls) {
               compute_s(smem + S * TILE, sA);
@@ -555,7 +537,7 @@ __global__ __launch_bounds__(NR * NS * 64, RA_BF16_OCC) void k_attn_bf16(AttnArg
         // skipped tiles of a row group: all of them less those its wavefronts visited (in the
         // paired mode the group's first wavefront adds the group's tiles, every one subtracts
         // its own; the unsigned sum wraps to the group's count)
-        const uint64_t own = PAIRED ? (pw_idx == 0 ? (uint64_t)ntk_all : 0) : (uint64_t)split_count(ntk_all);
+        const uint64_t own = PAIRED ? (pw_idx == 0 ? (uint64_t)ntk_all : 0) : (uint64_t)my_tiles(ntk_all);
         atomicAdd((unsigned long long*)&st->tiles_skipped, (unsigned long long)(own - st_full - st_diag));
       }
     }
@@ -649,11 +631,12 @@ __global__ __launch_bounds__(NR * NS * 64, RA_BF16_OCC) void k_attn_bf16(AttnArg
     }
   }
 
-  // ---- finalize: O = acc / l, LSE = ln(2) * (m + log2 l); rows with no key: 0 and -inf
+  // ---- finalize: O = acc / l, LSE = ln(2) * (m + log2 l); rows with no key: 0 and -inf (a NaN
+  // normaliser, from NaN inputs, counts as live so that the NaN reaches O and LSE)
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = pair_sum(l[qb]);
-    const bool live = lt > 0.f;
+    const bool live = !(lt <= 0.f);
     const float inv = live ? 1.f / lt : 0.f;
     const int y = qw0 + qb * 32 + l32;
     if (y < c) {

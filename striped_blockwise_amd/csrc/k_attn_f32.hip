@@ -56,10 +56,7 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
     const int k = ring_block(p, r, a.P);
     const int mode = round_mode(a.layout, a.causal, p, k);
     const int delta = mode == MODE_STRICT ? 1 : 0;
-    int ntk = ntk_all;
-    if (mode == MODE_SKIP) ntk = 0;
-    else if (mode != MODE_FULL) ntk = min(ntk_all, max(0, (q_last - delta) / TK + 1));
-    if (q_last - delta < 0 && mode != MODE_FULL) ntk = 0;
+    const int ntk = visited_tiles(mode, q_last, ntk_all, TK);
 
     const float* kp = (const float*)a.k + bh * a.kv_bh_stride + (int64_t)(k - a.kv_base) * a.kv_blk_stride;
     const float* vp = (const float*)a.v + bh * a.kv_bh_stride + (int64_t)(k - a.kv_base) * a.kv_blk_stride;
@@ -120,7 +117,7 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
   }
 
   if (y < c) {
-    const bool live = l > 0.f;
+    const bool live = !(l <= 0.f);        // NaN (from NaN inputs) propagates to O and LSE
     const float inv = live ? 1.f / l : 0.f;
     const int64_t oel = bh * a.o_bh_stride + dev * a.o_dev_stride + y * rstride;
     if (a.o_f32) {

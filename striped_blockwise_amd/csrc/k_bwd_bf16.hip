@@ -183,9 +183,7 @@ __global__ __launch_bounds__(NR * NS * 64, 2) void k_bwd_dq_bf16(BwdArgs a) {
     const int k = ring_block(p, r, a.P);
     const int mode = round_mode(a.layout, a.causal, p, k);
     const int delta = mode == MODE_STRICT ? 1 : 0;
-    int ntk = ntk_all;
-    if (mode == MODE_SKIP) ntk = 0;
-    else if (mode != MODE_FULL) ntk = (q_wg_last - delta < 0) ? 0 : min(ntk_all, (q_wg_last - delta) / TS + 1);
+    const int ntk = visited_tiles(mode, q_wg_last, ntk_all, TS);
     if (ntk == 0) continue;
 
     const int64_t kvo = bh * a.kv_bh_stride + (int64_t)(k - a.kv_base) * a.kv_blk_stride;
@@ -269,10 +267,10 @@ __global__ __launch_bounds__(NR * NS * 64, 2) void k_bwd_dq_bf16(BwdArgs a) {
       // This split's tiles: j = 0 .. my_n - 1 is tile j NS + s, in stage j & 1.  Wavefronts that
       // share tiles (NR > 1) run the workgroup's iteration count in lock-step; a lone wavefront
       // runs its own.  Only owned tiles are fetched: a split may own none in a round.
-      const int my_n = ntk > s ? (ntk - s + NS - 1) / NS : 0;
+      const int my_n = split_count(ntk, s, NS);
       const int nit = NR > 1 ? (ntk + NS - 1) / NS : my_n;
       auto issue = [&](int j, int stage) __attribute__((always_inline)) {
-        const int x0 = (j * NS + s) * TS;
+        const int x0 = split_tile(j, s, NS) * TS;
         dma_issue<NR, TS>(kdma, kblk, sb + stage * TILE, x0, c, a.row_step, g);
         dma_issue<NR, TS>(vdma, vblk, sb + (2 + stage) * TILE, x0, c, a.row_step, g);
       };
@@ -283,7 +281,7 @@ __global__ __launch_bounds__(NR * NS * 64, 2) void k_bwd_dq_bf16(BwdArgs a) {
         if (NR > 1) __syncthreads();                  // barrier also frees the other stage
         if (j + 1 < my_n) issue(j + 1, 1 - S);
         if (NR == 1 || j < my_n) {
-          const int t = j * NS + s;
+          const int t = split_tile(j, s, NS);
           const int cls = tile_class(t);
           if (cls) compute(smem + S * TILE, smem + (2 + S) * TILE, t, cls == 2);
         }
@@ -389,7 +387,7 @@ __global__ __launch_bounds__(RA_BWD_DKV_NW * 64, 2) void k_bwd_dkv_bf16(BwdArgs 
     const int delta = mode == MODE_STRICT ? 1 : 0;
     if (mode == MODE_SKIP) continue;
     // first query tile holding a row y >= x_wg0 + delta (a visible pair for some key here)
-    const int t0 = mode == MODE_FULL ? 0 : (x_wg0 + delta) / TS;
+    const int t0 = first_query_tile(mode, x_wg0, TS);
     if (t0 >= ntq) continue;
 
     const char* qblk = (const char*)((const __bf16*)a.q + bh * a.q_bh_stride + di * a.q_dev_stride);

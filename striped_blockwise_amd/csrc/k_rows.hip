@@ -143,6 +143,7 @@ __global__ __launch_bounds__(256) void k_merge(float* __restrict__ o_acc, float*
       wa = ea / sum;
       wb = eb / sum;
     }
+    if (la != la || lb != lb) wa = wb = L = la + lb;          // a NaN LSE on either side: NaN out
     float* oa = o_acc + row * d;
     const float* ob = o_part + row * d;
     if (vec4) {
@@ -203,6 +204,7 @@ __global__ __launch_bounds__(256) void k_merge_v4(float* __restrict__ o_acc, flo
         wa = ea / sum;
         wb = eb / sum;
       }
+      if (la[u] != la[u] || lb[u] != lb[u]) wa = wb = L = la[u] + lb[u];   // NaN LSE: NaN out
       f32x4v r;
 #pragma unroll
       for (int e = 0; e < 4; ++e) r[e] = wa * a[u][e] + wb * b[u][e];
@@ -422,7 +424,22 @@ int grid_for(uint64_t work_items, int per_block) {
   return g < 1 ? 1 : (int)g;
 }
 
+// Zero fill of n 64-bit words (the work counters that ra_forward overwrites).  A kernel rather
+// than hipMemsetAsync, so that a caller may capture the call in a HIP graph.
+__global__ __launch_bounds__(256) void k_zero_u64(uint64_t* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
 }  // namespace
+
+hipError_t launch_zero_u64(uint64_t* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_zero_u64, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_permute(const void* src, void* dst, int64_t BH, int64_t n, int64_t row_bytes,
                           int P, int inverse, hipStream_t s) {

@@ -111,6 +111,29 @@ bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
   return x < y + bbytes && y < x + abytes;
 }
 
+// A memory range [ptr, ptr + bytes) of one argument, for the aliasing checks.
+struct Span {
+  const void* p;
+  int64_t bytes;
+  const char* name;
+};
+
+// Every output span must be disjoint from every input span and from the other outputs (inputs
+// may alias each other: Q, K and V may be one tensor).
+template <size_t NO, size_t NI>
+ra_status_t check_no_alias(const Span (&outs)[NO], const Span (&ins)[NI]) {
+  for (size_t i = 0; i < NO; ++i) {
+    if (!outs[i].p || outs[i].bytes <= 0) continue;
+    for (size_t j = 0; j < NI; ++j)
+      if (ins[j].p && ins[j].bytes > 0 && overlaps(outs[i].p, outs[i].bytes, ins[j].p, ins[j].bytes))
+        return fail(RA_E_INVAL, "output %s overlaps input %s", outs[i].name, ins[j].name);
+    for (size_t j = i + 1; j < NO; ++j)
+      if (outs[j].p && outs[j].bytes > 0 && overlaps(outs[i].p, outs[i].bytes, outs[j].p, outs[j].bytes))
+        return fail(RA_E_INVAL, "outputs %s and %s overlap", outs[i].name, outs[j].name);
+  }
+  return ok();
+}
+
 ra_status_t check_bwd_support(const ra_problem_t* pr) {
   const bool sup = pr->dtype == RA_BF16 ? ra::bwd_bf16_supported(pr->d) : ra::bwd_f32_supported(pr->d);
   if (!sup)
@@ -236,6 +259,16 @@ ra_status_t ra_round(const ra_problem_t* prob, const void* q, const void* k, con
   if (prob->B * prob->H > 1 && (q_stride_bh < c * d || kv_stride_bh < c * d))
     return fail(RA_E_INVAL, "strides must be at least c*d = %lld elements", (long long)(c * d));
   if (stats && !aligned(stats, 8)) return fail(RA_E_INVAL, "stats must be 8-byte aligned");
+  {
+    const int64_t BH = prob->B * prob->H;
+    const int64_t eb = elem_bytes(prob->dtype);
+    const int64_t qb = ((BH - 1) * q_stride_bh + c * d) * eb, kvb = ((BH - 1) * kv_stride_bh + c * d) * eb;
+    const Span outs[] = {{o_part, BH * c * d * 4, "o_part"}, {lse_part, BH * c * 4, "lse_part"},
+                         {stats, (int64_t)sizeof(ra_round_stats_t), "stats"}};
+    const Span ins[] = {{q, qb, "q"}, {k, kvb, "k"}, {v, kvb, "v"}};
+    st = check_no_alias(outs, ins);
+    if (st != RA_OK) return st;
+  }
   ra::AttnArgs a{};
   a.q = q; a.k = k; a.v = v;
   a.q_bh_stride = q_stride_bh; a.kv_bh_stride = kv_stride_bh;
@@ -293,6 +326,16 @@ ra_status_t ra_forward(const ra_problem_t* prob, const void* q, const void* k, c
     return fail(RA_E_INVAL, "o must be 16-byte (f32) or 8-byte (bf16) aligned, lse 4-byte aligned");
   if (stats && !aligned(stats, 8)) return fail(RA_E_INVAL, "stats must be 8-byte aligned");
   const int64_t ndev = p_end - p_begin;
+  {
+    const int64_t BH = prob->B * prob->H;
+    const int64_t in_b = BH * prob->n * d * elem_bytes(prob->dtype);
+    const int64_t orows = prob->layout == RA_STRIPED_TOKENS ? prob->n : ndev * c;
+    const Span outs[] = {{o, BH * orows * d * (o_dtype == RA_F32 ? 4 : 2), "o"}, {lse, BH * orows * 4, "lse"},
+                         {stats, (int64_t)prob->P * prob->P * (int64_t)sizeof(ra_round_stats_t), "stats"}};
+    const Span ins[] = {{q, in_b, "q"}, {k, in_b, "k"}, {v, in_b, "v"}};
+    st = check_no_alias(outs, ins);
+    if (st != RA_OK) return st;
+  }
   ra::AttnArgs a{};
   a.k = k; a.v = v;
   a.q_bh_stride = prob->n * d; a.kv_bh_stride = prob->n * d;
@@ -319,6 +362,13 @@ ra_status_t ra_forward(const ra_problem_t* prob, const void* q, const void* k, c
   a.scale = eff_scale(prob);
   a.o_f32 = o_dtype == RA_F32 ? 1 : 0;
   a.stats = stats; a.stats_single = 0;
+  if (stats) {
+    // the counts of rows p_begin..p_end-1 are this call's own: clear them on the stream first
+    st = hip_status(ra::launch_zero_u64(reinterpret_cast<uint64_t*>(stats + (int64_t)p_begin * prob->P),
+                                        ndev * prob->P * 4, (hipStream_t)stream),
+                    "counter clear launch");
+    if (st != RA_OK) return st;
+  }
   return launch_attn(prob, a, (hipStream_t)stream);
 }
 
@@ -372,6 +422,16 @@ ra_status_t ra_backward_round(const ra_problem_t* prob, const void* q, const voi
   const int64_t gbytes = BH * c * d * 4;
   st = check_grad_outputs(dq_acc, gbytes, dk_acc, dv_acc, gbytes);
   if (st != RA_OK) return st;
+  {
+    const int64_t eb = elem_bytes(prob->dtype);
+    const int64_t qb = ((BH - 1) * q_stride_bh + c * d) * eb, dob = ((BH - 1) * do_stride_bh + c * d) * eb;
+    const int64_t kvb = ((BH - 1) * kv_stride_bh + c * d) * eb, rb = ((BH - 1) * row_stride_bh + c) * 4;
+    const Span outs[] = {{dq_acc, gbytes, "dq_acc"}, {dk_acc, gbytes, "dk_acc"}, {dv_acc, gbytes, "dv_acc"}};
+    const Span ins[] = {{q, qb, "q"}, {k, kvb, "k"}, {v, kvb, "v"}, {dout, dob, "dout"}, {lse, rb, "lse"},
+                        {delta, rb, "delta"}};
+    st = check_no_alias(outs, ins);
+    if (st != RA_OK) return st;
+  }
   if (ra::round_mode(prob->layout, prob->causal, p, kv) == ra::MODE_SKIP) return ok();
   ra::BwdArgs a{};
   a.q = q; a.dout = dout; a.lse = lse; a.delta = delta; a.k = k; a.v = v;
@@ -414,6 +474,15 @@ ra_status_t ra_backward(const ra_problem_t* prob, const void* q, const void* k, 
   st = check_grad_outputs(dq, BH * m * d * 4, dk, dv, BH * prob->n * d * 4);
   if (st != RA_OK) return st;
   const int64_t eb = elem_bytes(prob->dtype);
+  {
+    const int64_t in_b = BH * prob->n * d * eb;
+    const Span outs[] = {{dq, BH * m * d * 4, "dq"}, {dk, BH * prob->n * d * 4, "dk"},
+                         {dv, BH * prob->n * d * 4, "dv"}};
+    const Span ins[] = {{q, in_b, "q"}, {k, in_b, "k"}, {v, in_b, "v"}, {dout, BH * m * d * eb, "dout"},
+                        {lse, BH * m * 4, "lse"}, {delta, BH * m * 4, "delta"}};
+    st = check_no_alias(outs, ins);
+    if (st != RA_OK) return st;
+  }
   ra::BwdArgs a{};
   a.k = k; a.v = v;
   a.q_bh_stride = prob->n * d; a.do_bh_stride = m * d; a.row_bh_stride = m; a.kv_bh_stride = prob->n * d;

@@ -5,30 +5,9 @@
 #include <stdint.h>
 
 #include "ra.h"
+#include "tile_deal.h"
 
 namespace ra {
-
-// Per-(query device, K/V block) mask class.  From the causal matrix (query position < key
-// position is masked; Striped Attention review, "核心公式") and the GetMask procedures
-// ("GetMask 函数"), in local indices y (query row of block p) and x (key row of block k):
-//   FULL   every pair visible   (non-causal; contiguous block from an earlier device)
-//   INCL   visible iff x <= y   (contiguous own block; striped block from device k <= p)
-//   STRICT visible iff x <  y   (striped block from device k > p)
-//   SKIP   nothing visible      (contiguous block from a later device)
-enum Mode : int { MODE_FULL = 0, MODE_INCL = 1, MODE_STRICT = 2, MODE_SKIP = 3 };
-
-__host__ __device__ inline int round_mode(int layout, int causal, int p, int k) {
-  if (!causal) return MODE_FULL;
-  if (layout == RA_CONTIGUOUS) return k < p ? MODE_FULL : (k == p ? MODE_INCL : MODE_SKIP);
-  return k <= p ? MODE_INCL : MODE_STRICT;
-}
-
-// Ring schedule (Ring Attention review, step 2): blocks move from rank i to rank i+1 each
-// round, so in round r device p holds the block that started on device (p - r) mod P.
-__host__ __device__ inline int ring_block(int p, int r, int P) {
-  int k = (p - r) % P;
-  return k < 0 ? k + P : k;
-}
 
 // Launch description for the attention kernels (one for ra_round, one for ra_forward).
 struct AttnArgs {
@@ -111,6 +90,7 @@ struct BwdArgs {
 
 hipError_t launch_permute(const void* src, void* dst, int64_t BH, int64_t n, int64_t row_bytes,
                           int P, int inverse, hipStream_t s);
+hipError_t launch_zero_u64(uint64_t* p, int64_t n, hipStream_t s);
 hipError_t launch_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
                         int64_t rows, int64_t d, hipStream_t s);
 hipError_t launch_rope_permute(const void* src, void* dst, const int64_t* pos, int64_t BH, int64_t n, int64_t d,

@@ -52,12 +52,14 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, kind: str, label: str = ""):
 
 
 # Gradients (backward pass) against the fp64 oracle.  float32: same bound as the forward.
-# bf16: the kernels round P and dS to bf16 (relative error <= 2^-9 each, RMS 2^-9/sqrt(3) ~ 1.1e-3
-# for round-to-nearest) before the fp32-accumulated MFMA sums, and take O / LSE from the bf16
-# forward (LSE within 1e-3), so a gradient tensor's relative Frobenius error is ~2e-3; the
-# bounds leave 5x room.  Max-abs is taken relative to the tensor's largest reference entry.
+# bf16: the kernels round P and dS to bf16 before the fp32-accumulated MFMA sums (relative error
+# <= 2^-9 each, RMS 2^-9/sqrt(3) ~ 1.1e-3 for round-to-nearest, independent from term to term),
+# and P is formed from the bf16 forward's LSE (within 1e-3 absolute, so P within ~1e-3
+# relative, the same for every key of a row).  Adding the two in quadrature gives ~1.5e-3 for a
+# gradient tensor's relative Frobenius error; measured 1.6-1.8e-3.  The bound, 5e-3, is ~3x
+# that.  Max-abs is taken relative to the tensor's largest reference entry.
 F32_GRAD_ABS = 1e-4
-BF16_GRAD_RELFRO = 1e-2
+BF16_GRAD_RELFRO = 5e-3
 BF16_GRAD_MAXREL = 2e-2
 
 

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(ra):
 
 
 def test_abi_version_and_tiles(ra):
-    assert ra.abi_version() == 4
+    assert ra.abi_version() == 5
     tq, tk = ra.tile_shape(ra.BF16, 128)
     assert tq > 0 and tk > 0 and tq % 32 == 0 and tk % 16 == 0
     assert ra.tile_shape(ra.F32, 64)[0] > 0
@@ -236,3 +236,76 @@ def test_binding_offers_every_c_entry_point_by_name(ra):
             continue
         assert callable(getattr(ra, name, None)), name
         assert name in ra.__all__, name
+
+
+def test_outputs_may_not_alias_inputs(ra):
+    """Every attention and gradient entry point refuses outputs that overlap an input or another
+    output, on the host, before anything is launched.  The addresses are never dereferenced:
+    each call fails validation first."""
+    L = ra.lib()
+    V = ctypes.c_void_p
+    MB = 1 << 20
+    base = [V(0x40000000 + i * 64 * MB) for i in range(12)]      # disjoint 64 MB ranges
+    q, k, v, o, lse, st, do, de, dq, dk, dv, x = base
+    inside = lambda p, off=4096: V(p.value + off)
+    pr = ra._problem(1, 2, 256, 128, 4, ra.BF16, ra.STRIPED, True, 0.0)
+    c, d = 64, 128
+    # ra_round: o_part inside q, lse_part inside v, stats inside k, o_part over lse_part
+    assert L.ra_round(ctypes.byref(pr), q, k, v, c * d, c * d, 1, 0, inside(q), lse, None, None) == -1
+    assert b"o_part overlaps input q" in L.ra_last_error()
+    assert L.ra_round(ctypes.byref(pr), q, k, v, c * d, c * d, 1, 0, o, inside(v), None, None) == -1
+    assert b"lse_part overlaps input v" in L.ra_last_error()
+    assert L.ra_round(ctypes.byref(pr), q, k, v, c * d, c * d, 1, 0, o, lse, inside(k, 256), None) == -1
+    assert b"stats overlaps input k" in L.ra_last_error()
+    assert L.ra_round(ctypes.byref(pr), q, k, v, c * d, c * d, 1, 0, o, inside(o, 1024), None, None) == -1
+    assert b"outputs o_part and lse_part overlap" in L.ra_last_error()
+    # ra_forward: o inside k; lse inside q; stats inside o; q == k == v is allowed (checked on a
+    # failing call: the only error left is the stats overlap)
+    assert L.ra_forward(ctypes.byref(pr), q, k, v, 0, 4, inside(k), ra.BF16, lse, None, None) == -1
+    assert b"o overlaps input k" in L.ra_last_error()
+    assert L.ra_forward(ctypes.byref(pr), q, k, v, 0, 4, o, ra.BF16, inside(q, 64 * 1024 - 4), None, None) == -1
+    assert b"lse overlaps input q" in L.ra_last_error()
+    assert L.ra_forward(ctypes.byref(pr), q, q, q, 0, 4, o, ra.BF16, lse, inside(o, 8), None) == -1
+    assert b"outputs o and stats overlap" in L.ra_last_error()
+    tok = ra._problem(1, 2, 256, 128, 4, ra.BF16, ra.STRIPED_TOKENS, True, 0.0)
+    assert L.ra_forward(ctypes.byref(tok), q, k, v, 3, 4, inside(v, 2 * 256 * 128 * 2 - 8), ra.BF16, lse,
+                        None, None) == -1                        # token order: o spans all n rows
+    assert b"o overlaps input v" in L.ra_last_error()
+    # ra_backward: dq inside dout, dk inside lse, dv inside q
+    args = lambda **kw: [kw.get(n, dflt) for n, dflt in (("q", q), ("k", k), ("v", v), ("do", do), ("lse", lse),
+                                                          ("de", de))]
+    assert L.ra_backward(ctypes.byref(pr), *args(), 0, 4, inside(do), dk, dv, None) == -1
+    assert b"dq overlaps input dout" in L.ra_last_error()
+    assert L.ra_backward(ctypes.byref(pr), *args(), 0, 4, dq, inside(lse, 0), dv, None) == -1
+    assert b"dk overlaps input lse" in L.ra_last_error()
+    assert L.ra_backward(ctypes.byref(pr), *args(), 0, 4, dq, dk, inside(q), None) == -1
+    assert b"dv overlaps input q" in L.ra_last_error()
+    # ra_backward_round: dv_acc inside k, dq_acc inside delta
+    assert L.ra_backward_round(ctypes.byref(pr), *args(), c * d, c * d, c * d, c, 1, 0, dq, dk, inside(k),
+                               None) == -1
+    assert b"dv_acc overlaps input k" in L.ra_last_error()
+    assert L.ra_backward_round(ctypes.byref(pr), *args(), c * d, c * d, c * d, c, 1, 0, inside(de, 0), dk, dv,
+                               None) == -1
+    assert b"dq_acc overlaps input delta" in L.ra_last_error()
+
+
+def test_bench_imports_the_oracle_only_in_cpu_baseline():
+    """bench.py measures the product; the oracle is only timed, in the cpu_baseline leg."""
+    import ast
+    src = open(os.path.join(ROOT, "bench.py"), encoding="utf-8").read()
+    tree = ast.parse(src)
+    top = [n for n in tree.body if isinstance(n, (ast.Import, ast.ImportFrom))]
+    for n in top:
+        mods = [a.name for a in n.names] if isinstance(n, ast.Import) else [n.module or ""]
+        assert not any(m == "oracle" or m.startswith("oracle.") for m in mods), "module-level oracle import"
+    for fn in ast.walk(tree):
+        if not isinstance(fn, ast.FunctionDef):
+            continue
+        for n in ast.walk(fn):
+            mods = []
+            if isinstance(n, ast.Import):
+                mods = [a.name for a in n.names]
+            elif isinstance(n, ast.ImportFrom):
+                mods = [n.module or ""]
+            if any(m == "oracle" or m.startswith("oracle.") for m in mods):
+                assert fn.name == "cpu_baseline", f"{fn.name} imports the oracle"

@@ -115,27 +115,38 @@ def test_share256k_device7(ra, share, layout):
 
 
 def test_share256k_device7_token_order(ra, share):
-    """The timed step: device 7's share read straight from the token-order tensors
-    (RA_STRIPED_TOKENS).  Bit-exact against the permuted path, sampled rows against the oracle."""
+    """The timed step exactly as bench.py launches it: device 7's share read straight from the
+    token-order tensors (RA_STRIPED_TOKENS), no counters, preallocated outputs.  Bit-exact
+    against the permuted path, sampled rows against the oracle.  Then the counting variant of
+    the same launch, with a counter buffer pre-filled with garbage: the call clears device 7's
+    row and writes the closed-form counts there, leaves the other rows alone, and its O and LSE
+    equal the non-counting launch's bit for bit."""
     w, q, k, v = share
     P, c, p = w.P, w.c, w.device
-    stats = ra.new_stats(P)
-    o, lse = ra.forward(q, k, v, P, "striped_tokens", True, p_begin=p, p_end=p + 1, stats=stats)
+    o = torch.empty((w.B, w.H, w.n, w.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.H, w.n), dtype=torch.float32, device="cuda")
+    ra.forward(q, k, v, P, "striped_tokens", True, p_begin=p, p_end=p + 1, out=(o, lse))
     qs, ks, vs = (ra.permute(t, P) for t in (q, k, v))
     o_s, l_s = ra.forward(qs, ks, vs, P, "striped", True, p_begin=p, p_end=p + 1)
     del qs, ks, vs
     torch.cuda.synchronize()
     assert torch.equal(o[:, :, p::P], o_s) and torch.equal(lse[:, :, p::P], l_s), "token order vs permuted"
-    tq, tk = ra.tile_shape(ra.BF16, w.d)
-    got = stats.cpu().numpy()
-    assert np.array_equal(got[p], _expected_stats_row("striped", P, c, p, w.B * w.H, tq, tk)), got[p]
     rows = _sample_rows(c, seed=99)
     heads = [3, 17, 30]
     tokens = rows * P + p
     o_ref, l_ref = _oracle_rows(w, heads, tokens)
     compare(_sel(o, heads, tokens).float(), _sel(lse, heads, tokens), o_ref, l_ref, "bf16",
-            "share256k token order device 7")
-    del o, lse, o_s, l_s
+            "share256k token order device 7 (timed launch)")
+
+    stats = ra.new_stats(P).fill_(12345)
+    o2, l2 = ra.forward(q, k, v, P, "striped_tokens", True, p_begin=p, p_end=p + 1, stats=stats)
+    torch.cuda.synchronize()
+    tq, tk = ra.tile_shape(ra.BF16, w.d)
+    got = stats.cpu().numpy()
+    assert np.array_equal(got[p], _expected_stats_row("striped", P, c, p, w.B * w.H, tq, tk)), got[p]
+    assert (got[:p] == 12345).all() and (got[p + 1:] == 12345).all(), "rows of other devices were touched"
+    assert torch.equal(o2[:, :, p::P], o_s) and torch.equal(l2[:, :, p::P], l_s), "counting variant"
+    del o, lse, o2, l2, o_s, l_s
 
 
 def test_share256k_whole_sequence_equivariance(ra, share):
