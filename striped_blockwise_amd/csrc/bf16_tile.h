@@ -165,6 +165,14 @@ __device__ __forceinline__ bf16x8 read_a_tr_nowait(const char* __restrict__ tile
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// A plain LDS read through a restrict-qualified pointer, for the same reason as
+// read_a_tr_nowait: the compiler then does not make it wait for every LDS DMA in flight.  The
+// caller must have waited for the DMA that filled the data.
+template <typename T>
+__device__ __forceinline__ T lds_read_nowait(const char* __restrict__ base, int off) {
+  return *reinterpret_cast<const T*>(base + off);
+}
+
 // s_waitcnt with vmcnt(N) only (expcnt and lgkmcnt left at their maxima): at most N of this
 // thread's vector-memory loads, LDS DMA included, still outstanding.  They complete in order.
 template <int N>

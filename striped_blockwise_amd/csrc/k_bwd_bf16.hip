@@ -40,6 +40,9 @@ using namespace bf16t;
 #ifndef RA_BWD_DQ_NW
 #define RA_BWD_DQ_NW 8           // dQ kernel: wavefronts per workgroup (one workgroup per CU)
 #endif
+#ifndef RA_BWD_DQ_PAIR
+#define RA_BWD_DQ_PAIR 1         // dQ kernel: paired query tiles for wide launches with triangular rounds
+#endif
 #ifndef RA_BWD_DKV_NW
 #define RA_BWD_DKV_NW 4          // dK/dV kernel: wavefronts per workgroup (two per CU)
 #endif
@@ -47,6 +50,10 @@ constexpr int WR = 32;           // stationary rows per wavefront
 constexpr int TS = 32;           // streamed rows per tile
 constexpr int TILE = TS * ROWB;  // bytes of one streamed tile (8 KB)
 constexpr float NEG_BIG = -1e30f;  // clamp for L = -inf (a row that sees no key): P stays 0
+constexpr float NL_MAX = -NEG_BIG * LOG2E;   // the same clamp on -L log2(e)
+#ifndef RA_BWD_DKV_NOWAIT
+#define RA_BWD_DKV_NOWAIT 1      // dK/dV kernel: LDS reads without the compiler's wait for the next tile's DMA
+#endif
 
 // Block -> (stream, tile).  Blocks are dispatched round-robin over the 8 XCDs; with xcd_major
 // XCD x takes streams x, x+8, ... one after another, all tiles of a stream together, so the
@@ -106,8 +113,17 @@ __device__ __forceinline__ void store_rows(float* row, const f32x16 (&acc)[4], f
 // of a row group takes the K/V tiles s, s + NS, ... of every round into LDS stages of its own
 // (shared by its NR wavefronts), and the splits' dQ partial sums are added up through LDS at the
 // end: grids too small to fill the chip then spread each row group's sweep over its keys.
-template <int NR, int NS>
+//
+// PAIR (NS == 1, launches whose rounds are all causal-triangular): workgroup i of a stream takes
+// the query tiles i and nqt - 1 - i and, round by round, sweeps the round's K/V block for the
+// first tile and then for the second, adding each (round, tile) partial into dq as it goes.
+// Under triangular masks the two tiles see few and many keys, so every paired workgroup does
+// about the same work in every round: the workgroups resident at one time stay in the same
+// round and read the same K/V block, instead of drifting over all P blocks (whose union does
+// not fit the caches).  The query tile's Q, dO, L and D are reloaded for each sweep.
+template <int NR, int NS, bool PAIR>
 __global__ __launch_bounds__(NR * NS * 64, 2) void k_bwd_dq_bf16(BwdArgs a) {
+  static_assert(!PAIR || NS == 1, "paired query tiles: one key split");
   constexpr int NW = NR * NS;
   constexpr int WG_ROWS = NR * WR;      // stationary rows per workgroup
   constexpr int SPLIT_BYTES = 4 * TILE;                       // K0 K1 V0 V1 of one split
@@ -127,16 +143,12 @@ __global__ __launch_bounds__(NR * NS * 64, 2) void k_bwd_dq_bf16(BwdArgs a) {
   const int c = a.c;
 
   const int nqt = (c + WG_ROWS - 1) / WG_ROWS;
-  int stream, qt;
-  map_block(a.xcd_major, a.BH * a.n_dev, nqt, true, stream, qt);
+  int stream, unit;
+  // unpaired: heaviest query tile first (late rows see the most keys); paired: equal units
+  map_block(a.xcd_major, a.BH * a.n_dev, PAIR ? (nqt + 1) / 2 : nqt, !PAIR, stream, unit);
   const int bh = stream % a.BH;
   const int dev = stream / a.BH;
   const int p = a.p_begin + dev;
-  const int q_wg_last = min(c, qt * WG_ROWS + WG_ROWS) - 1;
-  const int qw0 = qt * WG_ROWS + g * WR;
-  const int qw_last = min(c, qw0 + WR) - 1;
-  const bool wave_live = qw0 < c;
-  const int y = qw0 + l32;
 
   int k_row[8], v_row[8], k_tr[4][2];
 #pragma unroll
@@ -154,37 +166,58 @@ __global__ __launch_bounds__(NR * NS * 64, 2) void k_bwd_dq_bf16(BwdArgs a) {
   // Split workgroups read K^T without the compiler's wait for every LDS DMA in flight (their
   // own waits cover the tile), as the forward's small shapes do.
   constexpr bool TR_NOWAIT = NS > 1;
-
-  // B operands: this lane's query row of Q and dO, head dims 16 dk + 8 hh .. +7
   const int64_t rstride = (int64_t)a.row_step * D;   // elements between rows of a block
-  const __bf16* qp = (const __bf16*)a.q + bh * a.q_bh_stride + dev * a.q_dev_stride + y * rstride + hh * 8;
-  const __bf16* dop = (const __bf16*)a.dout + bh * a.do_bh_stride + dev * a.do_dev_stride + y * rstride + hh * 8;
-  bf16x8 qf[8], df[8];
-#pragma unroll
-  for (int dk = 0; dk < 8; ++dk) {
-    qf[dk] = load_row8(qp + dk * 16, y < c);
-    df[dk] = load_row8(dop + dk * 16, y < c);
-  }
-  float nl = 0.f, dl = 0.f;    // -L log2(e) and D of this lane's row
-  if (y < c) {
-    const int64_t ro = bh * a.row_bh_stride + dev * a.row_dev_stride + (int64_t)y * a.row_step;
-    nl = -fmaxf(a.lse[ro], NEG_BIG) * LOG2E;
-    dl = a.delta[ro];
-  }
   const float cs = a.scale * LOG2E;
+
+  // The current query tile: its rows, and this lane's row of Q and dO (B operands, head dims
+  // 16 dk + 8 hh .. +7), -L log2(e) and D.
+  int qt = 0, q_wg_last = -1, qw0 = 0, qw_last = -1, y = 0;
+  bool wave_live = false;
+  bf16x8 qf[8], df[8];
+  float nl = 0.f, dl = 0.f;
+  auto set_tile = [&](int t) {
+    qt = t;
+    q_wg_last = min(c, qt * WG_ROWS + WG_ROWS) - 1;
+    qw0 = qt * WG_ROWS + g * WR;
+    qw_last = min(c, qw0 + WR) - 1;
+    wave_live = qw0 < c;
+    y = qw0 + l32;
+  };
+  auto load_tile = [&]() {
+    const __bf16* qp = (const __bf16*)a.q + bh * a.q_bh_stride + dev * a.q_dev_stride + y * rstride + hh * 8;
+    const __bf16* dop = (const __bf16*)a.dout + bh * a.do_bh_stride + dev * a.do_dev_stride + y * rstride + hh * 8;
+#pragma unroll
+    for (int dk = 0; dk < 8; ++dk) {
+      qf[dk] = load_row8(qp + dk * 16, y < c);
+      df[dk] = load_row8(dop + dk * 16, y < c);
+    }
+    nl = 0.f;
+    dl = 0.f;
+    if (y < c) {
+      const int64_t ro = bh * a.row_bh_stride + dev * a.row_dev_stride + (int64_t)y * a.row_step;
+      nl = -fmaxf(a.lse[ro], NEG_BIG) * LOG2E;
+      dl = a.delta[ro];
+    }
+  };
 
   f32x16 acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) acc[db] = f32x16{};
 
   const int ntk_all = (c + TS - 1) / TS;
-  for (int rr = 0; rr < a.r_count; ++rr) {
+  // Key tiles that the current query tile visits in ring round r_begin + rr.
+  auto round_tiles = [&](int rr) {
+    return visited_tiles(round_mode(a.layout, a.causal, p, ring_block(p, a.r_begin + rr, a.P)), q_wg_last,
+                         ntk_all, TS);
+  };
+  // The current query tile against the K/V block of round r_begin + rr, added into acc.
+  auto sweep_round = [&](int rr) __attribute__((always_inline)) {
     const int r = a.r_begin + rr;
     const int k = ring_block(p, r, a.P);
     const int mode = round_mode(a.layout, a.causal, p, k);
     const int delta = mode == MODE_STRICT ? 1 : 0;
     const int ntk = visited_tiles(mode, q_wg_last, ntk_all, TS);
-    if (ntk == 0) continue;
+    if (ntk == 0) return;
 
     const int64_t kvo = bh * a.kv_bh_stride + (int64_t)(k - a.kv_base) * a.kv_blk_stride;
     const char* kblk = (const char*)((const __bf16*)a.k + kvo);
@@ -294,7 +327,35 @@ __global__ __launch_bounds__(NR * NS * 64, 2) void k_bwd_dq_bf16(BwdArgs a) {
       if (j < nit) iter(j, std::integral_constant<int, 0>{});
       if (NR > 1) __syncthreads();                    // LDS stages free for the next round
     }
+  };
+
+  if constexpr (PAIR) {
+    // Per round: the first query tile's sweep, then the second's; each (round, tile) partial
+    // is scaled and added into dq (the first one written, unless accumulating).
+    const int pair[2] = {unit, nqt - 1 - unit};
+    const int nseg = pair[1] != pair[0] ? 2 : 1;
+    for (int rr = 0; rr < a.r_count; ++rr) {
+      for (int sg = 0; sg < nseg; ++sg) {
+        set_tile(pair[sg]);
+        const bool first = rr == 0 && a.accumulate == 0;
+        const bool work = round_tiles(rr) > 0;
+        if (!work && !first) continue;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) acc[db] = f32x16{};
+        if (work) {                                     // (no key in the first round: zeros)
+          load_tile();
+          sweep_round(rr);
+        }
+        if (y < c)
+          store_rows(a.dq + bh * a.dq_bh_stride + dev * a.dq_dev_stride + y * rstride, acc, a.scale, hh, !first);
+      }
+    }
+    return;
   }
+
+  set_tile(unit);
+  load_tile();
+  for (int rr = 0; rr < a.r_count; ++rr) sweep_round(rr);
 
   // Key splits: splits 1 .. NS-1 hand their dQ partial sums to split 0 of their row group
   // through LDS; split 0 adds them up and stores.
@@ -430,16 +491,26 @@ __global__ __launch_bounds__(RA_BWD_DKV_NW * 64, 2) void k_bwd_dkv_bf16(BwdArgs 
       int rwb = (int)(qs_ - smem) + rw0, trb = (int)(qs_ - smem) + tr0;
       asm volatile("" : "+v"(rwb), "+v"(trb));
       const int dq_o = (int)(os_ - qs_);
-      auto q_rowp = [&](int dk) { return smem + (rwb ^ (dk << 5)); };
-      auto o_rowp = [&](int dk) { return smem + ((rwb + dq_o) ^ (dk << 5)); };
-      auto q_tra = [&](int ks, int db) { return read_a_tr(smem, (trb + ks * 16 * ROWB) ^ tr_xor(db, 0), (trb + ks * 16 * ROWB) ^ tr_xor(db, 1)); };
-      auto o_tra = [&](int ks, int db) { return read_a_tr(smem, (trb + dq_o + ks * 16 * ROWB) ^ tr_xor(db, 0), (trb + dq_o + ks * 16 * ROWB) ^ tr_xor(db, 1)); };
+      // The tile's DMA was waited for at the barrier; the next tile's, issued after it, fills
+      // the other stage, so these reads need not wait for it (RA_BWD_DKV_NOWAIT).
+      constexpr bool NW_ = RA_BWD_DKV_NOWAIT != 0;
+      auto rd16 = [&](int off) -> bf16x8 {
+        return NW_ ? lds_read_nowait<bf16x8>(smem, off) : *reinterpret_cast<const bf16x8*>(smem + off);
+      };
+      auto rdtr = [&](int lo, int hi) -> bf16x8 {
+        return NW_ ? read_a_tr_nowait(smem, lo, hi) : read_a_tr(smem, lo, hi);
+      };
+      auto rd4f = [&](const char* p) -> float4 {
+        return NW_ ? lds_read_nowait<float4>(p, 0) : *reinterpret_cast<const float4*>(p);
+      };
+      auto q_tra = [&](int ks, int db) { return rdtr((trb + ks * 16 * ROWB) ^ tr_xor(db, 0), (trb + ks * 16 * ROWB) ^ tr_xor(db, 1)); };
+      auto o_tra = [&](int ks, int db) { return rdtr((trb + dq_o + ks * 16 * ROWB) ^ tr_xor(db, 0), (trb + dq_o + ks * 16 * ROWB) ^ tr_xor(db, 1)); };
       f32x16 s = f32x16{};
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         bf16x8 qa[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) qa[j] = *reinterpret_cast<const bf16x8*>(q_rowp(4 * h2 + j));
+        for (int j = 0; j < 4; ++j) qa[j] = rd16(rwb ^ ((4 * h2 + j) << 5));
 #pragma unroll
         for (int j = 0; j < 4; ++j) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[j], kf[4 * h2 + j], s, 0, 0, 0);
       }
@@ -452,14 +523,16 @@ __global__ __launch_bounds__(RA_BWD_DKV_NW * 64, 2) void k_bwd_dkv_bf16(BwdArgs 
           s[rg] = vis ? s[rg] : -INFINITY;
         }
       }
-      // P for rows acc_row(rg, hh): four runs of 4 consecutive rows of L
+      // P for rows acc_row(rg, hh): four runs of 4 consecutive rows of L.  -L log2(e) is clamped
+      // after the multiply (min of a product needs no NaN canonicalisation, max of a loaded
+      // value does); the same value as clamping L first.
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float4 l4 = *reinterpret_cast<const float4*>(rs_ + (8 * g + 4 * hh) * 4);
+        const float4 l4 = rd4f(rs_ + (8 * g + 4 * hh) * 4);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          s[4 * g + j] = __builtin_amdgcn_exp2f(fmaf(s[4 * g + j], cs, -fmaxf(lv[j], NEG_BIG) * LOG2E));
+          s[4 * g + j] = __builtin_amdgcn_exp2f(fmaf(s[4 * g + j], cs, fminf(-lv[j] * LOG2E, NL_MAX)));
       }
       {
         const bf16x8 p0 = pack8([&](int r) { return s[r]; }, 0);
@@ -477,13 +550,13 @@ __global__ __launch_bounds__(RA_BWD_DKV_NW * 64, 2) void k_bwd_dkv_bf16(BwdArgs 
       for (int h2 = 0; h2 < 2; ++h2) {
         bf16x8 oa[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) oa[j] = *reinterpret_cast<const bf16x8*>(o_rowp(4 * h2 + j));
+        for (int j = 0; j < 4; ++j) oa[j] = rd16((rwb + dq_o) ^ ((4 * h2 + j) << 5));
 #pragma unroll
         for (int j = 0; j < 4; ++j) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[j], vf[4 * h2 + j], dp, 0, 0, 0);
       }
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float4 d4 = *reinterpret_cast<const float4*>(rs_ + TS * 4 + (8 * g + 4 * hh) * 4);
+        const float4 d4 = rd4f(rs_ + TS * 4 + (8 * g + 4 * hh) * 4);
         const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) dp[4 * g + j] = s[4 * g + j] * (dp[4 * g + j] - dv[j]);
@@ -529,16 +602,31 @@ bool bwd_bf16_supported(int64_t d) { return d == D; }
 
 namespace {
 
-template <int NR, int NS>
+template <int NR, int NS, bool PAIR = false>
 hipError_t launch_dq(const BwdArgs& a, hipStream_t s) {
   constexpr int rows = NR * WR, nt = NR * NS * 64;
   const int64_t nstream = (int64_t)a.BH * a.n_dev;
-  const int64_t blocks = (a.c + rows - 1) / rows * nstream;
+  const int64_t nqt = (a.c + rows - 1) / rows;
+  const int64_t blocks = (PAIR ? (nqt + 1) / 2 : nqt) * nstream;
   if (blocks * nt >= (1ll << 32)) return hipErrorInvalidConfiguration;
   BwdArgs b = a;
   b.xcd_major = nstream % 8 == 0 ? 1 : 0;
-  hipLaunchKernelGGL((k_bwd_dq_bf16<NR, NS>), dim3((unsigned)blocks), dim3(nt), 0, s, b);
+  hipLaunchKernelGGL((k_bwd_dq_bf16<NR, NS, PAIR>), dim3((unsigned)blocks), dim3(nt), 0, s, b);
   return hipGetLastError();
+}
+
+// True when every round of the launch is causal-triangular for every launched device: causal,
+// and no contiguous round brings a block from an earlier device (k < p), which every query row
+// sees whole.
+bool all_rounds_triangular(const BwdArgs& a) {
+  if (!a.causal) return false;
+  if (a.layout != RA_CONTIGUOUS) return true;
+  for (int dv = 0; dv < a.n_dev; ++dv)
+    for (int i = 0; i < a.r_count; ++i) {
+      const int p = a.p_begin + dv;
+      if (round_mode(a.layout, a.causal, p, ring_block(p, a.r_begin + i, a.P)) == MODE_FULL) return false;
+    }
+  return true;
 }
 
 }  // namespace
@@ -563,7 +651,9 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int d, bool dq, bool dkv, hipStream
     const int64_t cus = cu_count();
     constexpr int WIDE_ROWS = RA_BWD_DQ_NW * WR;
     const int64_t wide = (int64_t)((a.c + WIDE_ROWS - 1) / WIDE_ROWS) * a.BH * a.n_dev;
-    if (wide >= 2 * cus) return launch_dq<RA_BWD_DQ_NW, 1>(a, s);
+    if (wide >= 2 * cus)
+      return RA_BWD_DQ_PAIR && all_rounds_triangular(a) ? launch_dq<RA_BWD_DQ_NW, 1, true>(a, s)
+                                                        : launch_dq<RA_BWD_DQ_NW, 1>(a, s);
     const int64_t groups = (int64_t)((a.c + WR - 1) / WR) * a.BH * a.n_dev;
     if (groups <= 4 * cus) return launch_dq<2, 4>(a, s);
     return launch_dq<4, 2>(a, s);
