@@ -145,7 +145,7 @@ __global__ __launch_bounds__(NR * NS * 64, 2) void k_bwd_dq_bf16(BwdArgs a) {
   const int nqt = (c + WG_ROWS - 1) / WG_ROWS;
   int stream, unit;
   // unpaired: heaviest query tile first (late rows see the most keys); paired: equal units
-  map_block(a.xcd_major, a.BH * a.n_dev, PAIR ? (nqt + 1) / 2 : nqt, !PAIR, stream, unit);
+  map_block(a.xcd_major, a.BH * a.n_dev, PAIR ? pair_count(nqt) : nqt, !PAIR, stream, unit);
   const int bh = stream % a.BH;
   const int dev = stream / a.BH;
   const int p = a.p_begin + dev;
@@ -332,7 +332,7 @@ __global__ __launch_bounds__(NR * NS * 64, 2) void k_bwd_dq_bf16(BwdArgs a) {
   if constexpr (PAIR) {
     // Per round: the first query tile's sweep, then the second's; each (round, tile) partial
     // is scaled and added into dq (the first one written, unless accumulating).
-    const int pair[2] = {unit, nqt - 1 - unit};
+    const int pair[2] = {unit, pair_second(unit, nqt)};
     const int nseg = pair[1] != pair[0] ? 2 : 1;
     for (int rr = 0; rr < a.r_count; ++rr) {
       for (int sg = 0; sg < nseg; ++sg) {
@@ -607,7 +607,7 @@ hipError_t launch_dq(const BwdArgs& a, hipStream_t s) {
   constexpr int rows = NR * WR, nt = NR * NS * 64;
   const int64_t nstream = (int64_t)a.BH * a.n_dev;
   const int64_t nqt = (a.c + rows - 1) / rows;
-  const int64_t blocks = (PAIR ? (nqt + 1) / 2 : nqt) * nstream;
+  const int64_t blocks = (PAIR ? pair_count((int)nqt) : nqt) * nstream;
   if (blocks * nt >= (1ll << 32)) return hipErrorInvalidConfiguration;
   BwdArgs b = a;
   b.xcd_major = nstream % 8 == 0 ? 1 : 0;

@@ -96,4 +96,10 @@ RA_HD void paired_deal(int idx, int k, int pbase, int ntk, int& t0, int& cnt) {
   cnt = t0 < ntk ? (ntk - t0 + k - 1) / k : 0;
 }
 
+// Paired query tiles (the dQ kernel under triangular masks): unit u of a stream's
+// pair_count(nqt) units takes the query tiles u and nqt - 1 - u (the same tile twice for the
+// middle unit of an odd count), so that every tile is taken exactly once.
+RA_HD int pair_count(int nqt) { return (nqt + 1) / 2; }
+RA_HD int pair_second(int u, int nqt) { return nqt - 1 - u; }
+
 }  // namespace ra

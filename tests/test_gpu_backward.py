@@ -274,3 +274,27 @@ def test_backward_dq_workgroup_shapes(ra, H, P, c):
         got = tuple(t.index_select(1, idx) for t in (dq, dk, dv))
         ref = _oracle(*(t[:, heads].contiguous() for t in (ql, kl, vl, gl)), P, order, True)
         _check(got, ref, "bf16", f"H={H} c={c} {layout}")
+
+
+@pytest.mark.parametrize("layout,H,P,c,p_begin,p_end", [
+    ("striped", 128, 2, 700, 0, 2),          # 3 query tiles of 256 rows: pairs (0, 2) and (1, 1)
+    ("striped", 64, 4, 1100, 1, 4),          # 5 tiles, three devices, ragged last tile
+    ("contiguous", 128, 2, 1500, 0, 1),      # device 0 alone: diagonal round, then a skipped one
+])
+def test_backward_dq_paired_query_tiles(ra, layout, H, P, c, p_begin, p_end):
+    """Wide dQ launches whose rounds are all causal-triangular pair query tiles i and nqt-1-i in
+    one workgroup and add each (round, tile) partial into dq: an odd tile count (a tile paired
+    with itself), a device range, and a contiguous launch with a round that skips every key.
+    Gradients of three heads against the oracle."""
+    d = 128
+    n = P * c
+    gen = torch.Generator().manual_seed(9700 + H + c)
+    q, k, v, g = (torch.randn((1, H, n, d), generator=gen).mul(0.5 if i < 3 else 1.0).to(torch.bfloat16)
+                  for i in range(4))
+    heads = [0, 5, H - 1]
+    (ql, kl, vl, gl), order = _to_layout((q, k, v, g), P, layout)
+    dq, dk, dv = _gpu_fwd_bwd(ra, ql, kl, vl, gl, P, layout, True, p_begin, p_end)
+    idx = torch.tensor(heads, device="cuda")
+    got = tuple(t.index_select(1, idx) for t in (dq, dk, dv))
+    ref = _oracle(*(t[:, heads].contiguous() for t in (ql, kl, vl, gl)), P, order, True, p_begin, p_end)
+    _check(got, ref, "bf16", f"paired dQ {layout} H={H} c={c} devices {p_begin}..{p_end - 1}")

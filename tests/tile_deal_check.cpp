@@ -176,6 +176,19 @@ static void check_key_side(int layout, int causal, int P, int c, int kblk, int p
   }
 }
 
+// dQ kernel, paired query tiles: every tile of a stream is taken by exactly one unit.
+static void check_query_pairs(int nqt) {
+  std::vector<int> seen(nqt, 0);
+  for (int u = 0; u < pair_count(nqt); ++u) {
+    const int a = u, b = pair_second(u, nqt);
+    CHECK(b >= a && b < nqt, "query pairs: unit %d of %d takes tiles %d and %d", u, nqt, a, b);
+    ++seen[a];
+    if (b != a) ++seen[b];
+  }
+  for (int t = 0; t < nqt; ++t) CHECK(seen[t] == 1, "query pairs: tile %d of %d taken %d times", t, nqt, seen[t]);
+  ++g_cases;
+}
+
 int main(int argc, char** argv) {
   const int c_max = argc > 1 ? std::atoi(argv[1]) : 700;
   const int Ps[] = {1, 2, 3, 4, 8, 64};
@@ -204,6 +217,7 @@ int main(int argc, char** argv) {
       }
     }
   }
+  for (int nqt = 1; nqt <= 1000; ++nqt) check_query_pairs(nqt);
   // the full-size shares: c = 32768 (P = 8 and 32), every device of P = 8
   for (int layout : layouts)
     for (int p = 0; p < 8; ++p) {
