@@ -53,11 +53,13 @@ def log(*a):
 
 
 class ClockSampler:
-    """Graphics clock and socket power of the GPU, sampled from the driver's metrics table
-    (amdsmi) in a host thread while a timed region runs.  Best effort: ``result()`` is None
-    when amdsmi is missing or refuses access."""
+    """Graphics clocks and socket power of the GPU while a kernel runs, from the driver's metrics
+    table (amdsmi).  The table refreshes about once a second, so the sampler polls it from a host
+    thread while the caller keeps the kernel running for a few seconds, and keeps only the fresh
+    entries (a new accumulation counter) that arrive inside that window.  Best effort: ``result()``
+    is None when amdsmi is missing or refuses access."""
 
-    def __init__(self, torch, dev, period_s: float = 0.01):
+    def __init__(self, torch, dev, period_s: float = 0.005):
         import threading
         self.samples = []
         self.period = period_s
@@ -65,6 +67,7 @@ class ClockSampler:
         self.thread = None
         self.handle = None
         self.err = None
+        self.window = None
         try:
             import amdsmi
             amdsmi.amdsmi_init()
@@ -81,51 +84,72 @@ class ClockSampler:
                     continue
             if self.handle is None and len(handles) == 1:
                 self.handle = handles[0]
+            try:
+                cap = amdsmi.amdsmi_get_power_cap_info(self.handle).get("power_cap")
+                self.cap_w = cap / 1e6 if isinstance(cap, (int, float)) and cap > 1e5 else cap
+            except Exception:
+                self.cap_w = None
         except Exception as e:  # pragma: no cover - depends on the box
             self.err = repr(e)
 
     def _read(self):
         m = self.smi.amdsmi_get_gpu_metrics_info(self.handle)
         clks = [x for x in (m.get("current_gfxclks") or []) if isinstance(x, (int, float)) and 0 < x < 10000]
-        clk = sum(clks) / len(clks) if clks else m.get("current_gfxclk")
+        if not clks and isinstance(m.get("current_gfxclk"), (int, float)):
+            clks = [m["current_gfxclk"]]
         pw = m.get("current_socket_power")
-        if not isinstance(pw, (int, float)) or pw <= 0 or pw > 100000:
-            pw = m.get("average_socket_power")
-        return clk, pw
+        return m.get("accumulation_counter"), clks, pw if isinstance(pw, (int, float)) and 0 < pw < 100000 else None
 
     def _run(self):
+        import time as _t
+        last = None
         while not self.stop_ev.is_set():
             try:
-                self.samples.append(self._read())
+                acc, clks, pw = self._read()
             except Exception as e:  # pragma: no cover
                 self.err = repr(e)
                 return
+            if acc != last:
+                self.samples.append((_t.perf_counter(), clks, pw))
+                last = acc
             self.stop_ev.wait(self.period)
 
-    def start(self):
+    def run_while(self, torch, fn, seconds: float = 3.0):
+        """Keep calling fn() (enqueueing GPU work) for about `seconds`, sampling meanwhile."""
         import threading
+        import time as _t
         if self.handle is None:
             return self
         self.thread = threading.Thread(target=self._run, daemon=True)
         self.thread.start()
-        return self
-
-    def stop(self):
-        if self.thread is not None:
-            self.stop_ev.set()
-            self.thread.join()
+        fn()
+        torch.cuda.synchronize()
+        t0 = _t.perf_counter()                 # the GPU has been busy since just before here
+        while _t.perf_counter() - t0 < seconds:
+            fn()
+            fn()
+            torch.cuda.synchronize()
+        t1 = _t.perf_counter()
+        self.stop_ev.set()
+        self.thread.join()
+        self.window = (t0, t1)
         return self
 
     def result(self, cus: int):
-        clk = [c for c, _ in self.samples if isinstance(c, (int, float)) and 0 < c < 10000]
-        pw = [p for _, p in self.samples if isinstance(p, (int, float)) and 0 < p < 100000]
-        if not clk:
+        if self.window is None:
             return None if self.err is None else {"error": self.err}
-        mhz = sum(clk) / len(clk)
-        return {"sclk_mhz_mean": round(mhz, 1), "samples": len(clk),
-                "socket_power_w_mean": round(sum(pw) / len(pw), 1) if pw else None,
+        t0, t1 = self.window
+        fresh = [(c, p) for t, c, p in self.samples if t0 < t < t1 and c]
+        if not fresh:
+            return {"error": "no fresh metrics entry inside the window"}
+        mhz = sum(sum(c) / len(c) for c, _ in fresh) / len(fresh)
+        pw = [p for _, p in fresh if p]
+        return {"sclk_mhz_mean": round(mhz, 1), "fresh_samples": len(fresh),
+                "xcd_mhz_last": fresh[-1][0],
+                "socket_power_w_mean": round(sum(pw) / len(pw), 1) if pw else None, "power_cap_w": self.cap_w,
                 "peak_at_sclk_tflops": round(cus * mhz * 1e6 * 4096 / 1e12, 1),
-                "source": "amdsmi gpu_metrics current_gfxclk(s), sampled every 10 ms over the timed region"}
+                "source": "amdsmi gpu_metrics current_gfxclks (per XCD) and current_socket_power: the entries "
+                          "refreshed while the same forward ran back to back for ~3 s after the timed steps"}
 
 
 def useful_pairs(layout: str, P: int, c: int, p: int, causal: bool = True) -> list:
@@ -514,9 +538,7 @@ def main(argv=None) -> int:
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    sampler = ClockSampler(torch, dev)
     torch.cuda.synchronize()
-    sampler.start()
     wall0 = time.perf_counter()
     s0.record()
     for i in range(args.steps):
@@ -525,7 +547,6 @@ def main(argv=None) -> int:
     s1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    sampler.stop()
     step_mean = s0.elapsed_time(s1) / args.steps
     # the step is the one forward launch: its per-step event times, median over the K steps
     fwd_ms = sorted(a.elapsed_time(b) for a, b in ev)
@@ -534,12 +555,17 @@ def main(argv=None) -> int:
     value = flops_s / (step_ms * 1e-3) / 1e12
     achieved = flops_s / (fwd_avg * 1e-3) / 1e12
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    clock = sampler.result(cus)
+    # clocks and power while the same launch runs (outside the timed steps)
+    clock = ClockSampler(torch, dev).run_while(torch, lambda: ra.forward(
+        q, k, v, P, "striped_tokens", True, p_begin=p, p_end=p + 1, out=(o_t, lse_t))).result(cus)
     log(f"[bench] striped step median {step_ms:.2f} ms ({value:.1f} TFLOP/s), mean {step_mean:.2f} ms; forward "
         f"kernel mean {fwd_avg:.2f} ms ({achieved:.1f} TFLOP/s, {100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
     if clock and "sclk_mhz_mean" in clock:
-        log(f"[bench] sclk {clock['sclk_mhz_mean']:.0f} MHz, socket power {clock['socket_power_w_mean']} W: "
-            f"peak at that clock {clock['peak_at_sclk_tflops']:.0f} TFLOP/s")
+        log(f"[bench] sclk {clock['sclk_mhz_mean']:.0f} MHz ({clock['fresh_samples']} samples), socket power "
+            f"{clock['socket_power_w_mean']} W of {clock['power_cap_w']} W: peak at that clock "
+            f"{clock['peak_at_sclk_tflops']:.0f} TFLOP/s")
+    else:
+        log(f"[bench] clock: {clock}")
 
     result = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
@@ -721,8 +747,12 @@ def main(argv=None) -> int:
         b.record()
         torch.cuda.synchronize()
         gemm_ms = a.elapsed_time(b) / reps
+        gclock = ClockSampler(torch, dev).run_while(torch, lambda: [torch.matmul(ga, gb) for _ in range(20)]).result(cus)
         result["context_gemm"] = {"op": "torch.matmul bf16 8192x8192x8192 (hipBLASLt)", "ms": round(gemm_ms, 4),
-                                  "tflops": round(2.0 * g ** 3 / (gemm_ms * 1e-3) / 1e12, 1)}
+                                  "tflops": round(2.0 * g ** 3 / (gemm_ms * 1e-3) / 1e12, 1), "clock": gclock}
+        if gclock and gclock.get("peak_at_sclk_tflops"):
+            result["context_gemm"]["frac_of_peak_at_sclk"] = round(
+                result["context_gemm"]["tflops"] / gclock["peak_at_sclk_tflops"], 4)
         log(f"[bench] bf16 GEMM 8192^3: {result['context_gemm']['tflops']} TFLOP/s")
         del ga, gb
 
