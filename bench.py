@@ -45,7 +45,8 @@ PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published
 PMC_FILE = os.path.join(ROOT, "profiles", "k_attn_bf16_share_n256k_pmc.json")
 # the fused forward's sources: the counters in PMC_FILE are used only while these are unchanged
-KERNEL_SRCS = [os.path.join(ROOT, "striped_blockwise_amd", "csrc", f) for f in ("k_attn_bf16.hip", "bf16_tile.h")]
+KERNEL_SRCS = [os.path.join(ROOT, "striped_blockwise_amd", "csrc", f)
+               for f in ("k_attn_bf16.hip", "bf16_tile.h", "tile_deal.h")]
 
 
 def log(*a):
@@ -455,7 +456,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="share_n256k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="only the timed striped steps")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the timed striped steps (no other legs, no clock window): for profiler runs")
     ap.add_argument("--backward", action="store_true",
                     help="instead of the default line: backward (dQ, dK, dV) of the device share, both layouts")
     ap.add_argument("--sweep", action="store_true",
@@ -556,7 +558,7 @@ def main(argv=None) -> int:
     achieved = flops_s / (fwd_avg * 1e-3) / 1e12
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     # clocks and power while the same launch runs (outside the timed steps)
-    clock = ClockSampler(torch, dev).run_while(torch, lambda: ra.forward(
+    clock = None if args.no_extras else ClockSampler(torch, dev).run_while(torch, lambda: ra.forward(
         q, k, v, P, "striped_tokens", True, p_begin=p, p_end=p + 1, out=(o_t, lse_t))).result(cus)
     log(f"[bench] striped step median {step_ms:.2f} ms ({value:.1f} TFLOP/s), mean {step_mean:.2f} ms; forward "
         f"kernel mean {fwd_avg:.2f} ms ({achieved:.1f} TFLOP/s, {100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
