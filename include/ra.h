@@ -239,7 +239,9 @@ ra_status_t ra_backward_round(const ra_problem_t* prob, const void* q, const voi
  *   RA_STRIPED_TOKENS: every tensor in token order, with m = n: dout and dq [B, H, n, d],
  *            lse and delta [B, H, n]; dq is written only on the rows of the selected devices
  *            (tokens t with p_begin <= t mod P < p_end), dk and dv on every row.
- * Every output element is written exactly once, by one workgroup, in a fixed order. */
+ * Each output element belongs to one workgroup, which writes it in a fixed order (a dQ row may
+ * be stored after one round and added to after later rounds by that same workgroup); no
+ * atomics, so the results are the same from run to run. */
 ra_status_t ra_backward(const ra_problem_t* prob, const void* q, const void* k, const void* v,
                         const void* dout, const float* lse, const float* delta, int32_t p_begin,
                         int32_t p_end, float* dq, float* dk, float* dv, void* stream);

@@ -124,7 +124,6 @@ __device__ __forceinline__ void store_rows(float* row, const f32x16 (&acc)[4], f
 template <int NR, int NS, bool PAIR>
 __global__ __launch_bounds__(NR * NS * 64, 2) void k_bwd_dq_bf16(BwdArgs a) {
   static_assert(!PAIR || NS == 1, "paired query tiles: one key split");
-  constexpr int NW = NR * NS;
   constexpr int WG_ROWS = NR * WR;      // stationary rows per workgroup
   constexpr int SPLIT_BYTES = 4 * TILE;                       // K0 K1 V0 V1 of one split
   constexpr int SLOT = 64 * 64 * 4;                           // one wavefront's dQ partial
