@@ -150,7 +150,7 @@ class ClockSampler:
                 "socket_power_w_mean": round(sum(pw) / len(pw), 1) if pw else None, "power_cap_w": self.cap_w,
                 "peak_at_sclk_tflops": round(cus * mhz * 1e6 * 4096 / 1e12, 1),
                 "source": "amdsmi gpu_metrics current_gfxclks (per XCD) and current_socket_power: the entries "
-                          "refreshed while the same forward ran back to back for ~3 s after the timed steps"}
+                          "refreshed while the measured launch ran back to back for ~3 s after its timed runs"}
 
 
 def useful_pairs(layout: str, P: int, c: int, p: int, causal: bool = True) -> list:
