@@ -49,8 +49,10 @@ using namespace bf16t;
 constexpr int WR = 32;           // stationary rows per wavefront
 constexpr int TS = 32;           // streamed rows per tile
 constexpr int TILE = TS * ROWB;  // bytes of one streamed tile (8 KB)
-constexpr float NEG_BIG = -1e30f;  // clamp for L = -inf (a row that sees no key): P stays 0
-constexpr float NL_MAX = -NEG_BIG * LOG2E;   // the same clamp on -L log2(e)
+// dQ kernel: clamp for L = -inf (a row that sees no key), so that P stays 0 on its masked keys.
+// The dK/dV kernel needs none: its accumulator starts at -L / scale (+inf for such a row) and
+// the element mask sets every masked pair to -inf, which such a row's pairs all are.
+constexpr float NEG_BIG = -1e30f;
 #ifndef RA_BWD_DKV_NOWAIT
 #define RA_BWD_DKV_NOWAIT 1      // dK/dV kernel: LDS reads without the compiler's wait for the next tile's DMA
 #endif
@@ -435,6 +437,7 @@ __global__ __launch_bounds__(RA_BWD_DKV_NW * 64, 2) void k_bwd_dkv_bf16(BwdArgs 
     vf[dk] = load_row8((const __bf16*)a.v + kvo + dk * 16, x < c);
   }
   const float cs = a.scale * LOG2E;
+  const float nis = -1.0f / a.scale;
 
   f32x16 dka[4], dva[4];
 #pragma unroll
@@ -504,7 +507,18 @@ __global__ __launch_bounds__(RA_BWD_DKV_NW * 64, 2) void k_bwd_dkv_bf16(BwdArgs 
       };
       auto q_tra = [&](int ks, int db) { return rdtr((trb + ks * 16 * ROWB) ^ tr_xor(db, 0), (trb + ks * 16 * ROWB) ^ tr_xor(db, 1)); };
       auto o_tra = [&](int ks, int db) { return rdtr((trb + dq_o + ks * 16 * ROWB) ^ tr_xor(db, 0), (trb + dq_o + ks * 16 * ROWB) ^ tr_xor(db, 1)); };
-      f32x16 s = f32x16{};
+      // The accumulator starts at -L / scale for its row (acc_row(rg, hh): four runs of 4
+      // consecutive rows), so that the products leave S - L / scale, and the exp2 argument is one
+      // multiply by scale log2(e).
+      f32x16 s;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 l4 = rd4f(rs_ + (8 * g + 4 * hh) * 4);
+        s[4 * g] = l4.x * nis;
+        s[4 * g + 1] = l4.y * nis;
+        s[4 * g + 2] = l4.z * nis;
+        s[4 * g + 3] = l4.w * nis;
+      }
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         bf16x8 qa[4];
@@ -522,17 +536,11 @@ __global__ __launch_bounds__(RA_BWD_DKV_NW * 64, 2) void k_bwd_dkv_bf16(BwdArgs 
           s[rg] = vis ? s[rg] : -INFINITY;
         }
       }
-      // P for rows acc_row(rg, hh): four runs of 4 consecutive rows of L.  -L log2(e) is clamped
-      // after the multiply (min of a product needs no NaN canonicalisation, max of a loaded
-      // value does); the same value as clamping L first.
+      // P = exp2((S - L / scale) scale log2(e)).  A row that sees no key (L = -inf) has +inf
+      // here, but it has no visible pair, so every tile it meets takes the element mask above
+      // (or is skipped) and its pairs are -inf: P = 0.
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 l4 = rd4f(rs_ + (8 * g + 4 * hh) * 4);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          s[4 * g + j] = __builtin_amdgcn_exp2f(fmaf(s[4 * g + j], cs, fminf(-lv[j] * LOG2E, NL_MAX)));
-      }
+      for (int rg = 0; rg < 16; ++rg) s[rg] = __builtin_amdgcn_exp2f(s[rg] * cs);
       {
         const bf16x8 p0 = pack8([&](int r) { return s[r]; }, 0);
         const bf16x8 p1 = pack8([&](int r) { return s[r]; }, 1);
